@@ -1,0 +1,243 @@
+"""Pins of the oracle walk: brute force on the Fig. 2 toy shape, closed forms,
+tie-break, key order, resume invariance, recurrent update, bf16 projection."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from oracle.fp import bf16_to_f32, bf16_rne, tanh_p
+from fp32emu import rnd32, rnd_bf16, rint_even, f32_to_frac
+
+
+def _F(x):
+    return f32_to_frac(np.float32(x))
+
+
+def _brute_quant(u):
+    uf = [_F(x) for x in u]
+    amax = max(abs(x) for x in uf)
+    if amax == 0:
+        return [0] * len(u), [0] * len(u), Fraction(0), Fraction(0)
+    s_hi = rnd32(amax / 127)
+    inv = rnd32(Fraction(127) / amax)
+    inv256 = rnd32(inv * 256)
+    hi = [max(-127, min(127, rint_even(rnd32(x * inv)))) for x in uf]
+    lo = []
+    for x, h in zip(uf, hi):
+        res = rnd32(x - rnd32(s_hi * h))
+        lo.append(max(-127, min(127, rint_even(rnd32(res * inv256)))))
+    return hi, lo, s_hi, s_hi / 256
+
+
+def _brute_walk(d, temperature=0, seed=0, step_offset=0):
+    """Every operation of the int8 Markov / recurrent walk with exact rationals."""
+    W, s_w, E, base, x0 = d["W"], d["s_w"], d["E"], d["base"], d["x0"]
+    B, gamma, V = base.shape
+    r = W.shape[1]
+    toks = np.zeros((B, gamma), np.int64)
+    logits = np.zeros((B, gamma, V), np.uint16)
+    for b in range(B):
+        x = int(x0[b])
+        h = None if d["head"] == "markov" else [np.float32(v) for v in d["h0"][b]]
+        for t in range(gamma):
+            if d["head"] == "markov":
+                lat = E[x]
+            else:
+                A = bf16_to_f32(d["A"])
+                hn = []
+                for j in range(r):
+                    acc = Fraction(0)
+                    for k in range(r):
+                        acc = rnd32(acc + rnd32(_F(A[j, k]) * _F(h[k])))
+                    pre = rnd32(rnd32(acc + _F(E[x, j])) + _F(d["c"][j]))
+                    hn.append(tanh_p(np.float32(float(pre))))
+                h = hn
+                lat = np.array(h, np.float32)
+            hi, lo, s_hi, s_lo = _brute_quant(lat)
+            scores = []
+            for v in range(V):
+                ah = sum(int(W[v, k]) * hi[k] for k in range(r))
+                al = sum(int(W[v, k]) * lo[k] for k in range(r))
+                z = rnd32(rnd32(ah * s_hi) + rnd32(al * s_lo))
+                z = rnd32(z * _F(s_w[v]))
+                z = rnd32(z + _F(bf16_to_f32(base[b, t, v])))
+                lg = rnd_bf16(z)
+                logits[b, t, v] = bf16_rne(np.float32(float(lg)))
+                if temperature == 1:
+                    g = oracle.gumbel_noise(seed, b, step_offset + t, np.array([v]))[0]
+                    lg = rnd32(lg + _F(g))
+                scores.append((-lg, v))
+            x = min(scores)[1]
+            toks[b, t] = x
+    return toks, logits
+
+
+@pytest.mark.parametrize("temperature", [0, 1])
+@pytest.mark.parametrize("head", ["markov", "recurrent"])
+def test_toy_walk_brute_force(temperature, head):
+    # Fig. 2 toy shape: V=12, r=4, three steps (two batch rows)
+    d = datagen.make_inputs(12, 4, 2, 3, head=head, seed=11)
+    toks, lg = _brute_walk(d, temperature, seed=3)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head=head,
+                    A=d["A"], c=d["c"], h0=d["h0"], temperature=temperature, seed=3)
+    assert np.array_equal(o["tokens"], toks)
+    assert np.array_equal(o["logits"], lg)
+
+
+def test_toy_walk_brute_force_ties():
+    # bf16 base values drawn from a tiny set and E = 0 -> many exact ties at the top
+    d = datagen.make_inputs(12, 4, 1, 3, seed=12)
+    d["E"][:] = 0
+    d["E"][:, 0] = np.float32(1e-3)
+    d["base"][:] = bf16_rne(np.float32(1.0))
+    d["base"][0, 1, 5] = d["base"][0, 1, 9] = bf16_rne(np.float32(2.0))
+    toks, lg = _brute_walk(d)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"])
+    assert np.array_equal(o["tokens"], toks) and np.array_equal(o["logits"], lg)
+
+
+def test_project_int8_exact_bruteforce():
+    rng = np.random.default_rng(9)
+    W = rng.integers(-127, 128, size=(37, 256)).astype(np.int8)
+    hi = rng.integers(-127, 128, size=(2, 256)).astype(np.int8)
+    lo = rng.integers(-127, 128, size=(2, 256)).astype(np.int8)
+    ah, al = oracle.project_int8(W.astype(np.float64), hi, lo)
+    for b in range(2):
+        for v in range(37):
+            assert ah[b, v] == sum(int(W[v, k]) * int(hi[b, k]) for k in range(256))
+            assert al[b, v] == sum(int(W[v, k]) * int(lo[b, k]) for k in range(256))
+    # the worst case stays below 2^24, so the conversion to binary32 is exact
+    full = oracle.project_int8(np.full((1, 256), 127.0), np.full(256, 127, np.int8), np.full(256, -127, np.int8))
+    assert full[0][0] == 256 * 127 * 127 < 2 ** 24 and full[1][0] == -256 * 127 * 127
+
+
+def test_epilogue_matches_rational_emulation():
+    rng = np.random.default_rng(10)
+    n = 4000
+    ah = rng.integers(-4_129_024, 4_129_025, n)
+    al = rng.integers(-4_129_024, 4_129_025, n)
+    s_hi = np.float32(rng.uniform(1e-4, 1e-2))
+    s_lo = np.float32(s_hi / 256)
+    s_w = rng.uniform(1e-3, 0.1, n).astype(np.float32)
+    base = bf16_rne(rng.normal(0, 1.4, n).astype(np.float32))
+    lg, z = oracle.epilogue_int8(ah, al, s_hi, s_lo, s_w, base)
+    for i in range(n):
+        q = rnd32(rnd32(int(ah[i]) * _F(s_hi)) + rnd32(int(al[i]) * _F(s_lo)))
+        q = rnd32(q * _F(s_w[i]))
+        q = rnd32(q + _F(bf16_to_f32(base[i])))
+        assert Fraction(float(z[i])) == q
+        assert Fraction(float(bf16_to_f32(lg[i]))) == rnd_bf16(q)
+
+
+def test_select_and_key_order_with_ties():
+    rng = np.random.default_rng(11)
+    vals = np.array([0.0, -0.0, 1.5, -2.0, 1.5, 3.25, -0.0], np.float32)
+    for trial in range(200):
+        s = rng.choice(vals, size=rng.integers(1, 40)).astype(np.float32)
+        idx = np.arange(s.size)
+        lex = np.lexsort((idx, -s.astype(np.float64)))[0]
+        assert oracle.select_token(s) == lex == int(np.argmax(s))
+        keys = oracle.order_key(s, idx)
+        assert int(np.argmax(keys)) == lex
+    # -0 and +0 are equal: the lower index wins whichever sign it carries
+    assert oracle.select_token(np.array([-0.0, 0.0], np.float32)) == 0
+    assert oracle.select_token(np.array([0.0, -0.0], np.float32)) == 0
+    k = oracle.order_key(np.array([-0.0, 0.0], np.float32), np.array([5, 5]))
+    assert k[0] == k[1]
+    # key order: negative < -0 == +0 < positive; and below any finite key sits 0
+    k = oracle.order_key(np.array([-1e30, -1.0, 0.0, 1e-30, 2.0], np.float32), np.zeros(5, np.int64))
+    assert np.all(np.diff(k.astype(object)) > 0) and np.all(k > 0)
+
+
+def test_closed_form_zero_embedding_is_per_step_argmax():
+    d = datagen.make_inputs(300, 16, 3, 5, seed=13)
+    d["E"][:] = 0
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"])
+    want = np.argmax(bf16_to_f32(d["base"]), axis=-1)
+    assert np.array_equal(o["tokens"], want)
+    assert np.array_equal(o["logits"], d["base"])
+
+
+def test_closed_form_cyclic_successor():
+    V, r = 12, 4
+    th = 2 * np.pi * np.arange(V) / V
+    d = datagen.make_inputs(V, r, 4, 6, seed=14)
+    d["W"] = np.zeros((V, r), np.int8)
+    d["W"][:, 0] = np.rint(127 * np.cos(th))
+    d["W"][:, 1] = np.rint(127 * np.sin(th))
+    d["s_w"] = np.full(V, 1 / 127, np.float32)
+    d["E"] = np.zeros((V, r), np.float32)
+    d["E"][:, 0] = np.cos(np.roll(th, -1))
+    d["E"][:, 1] = np.sin(np.roll(th, -1))
+    d["base"][:] = 0
+    d["x0"] = np.array([0, 5, 11, 7], np.int32)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"])
+    want = (d["x0"][:, None] + np.arange(1, 7)[None, :]) % V
+    assert np.array_equal(o["tokens"], want)
+
+
+def test_closed_form_recurrent():
+    d = datagen.make_inputs(50, 8, 2, 4, head="recurrent", seed=15)
+    d["A"][:] = 0
+    d["c"][:] = 0
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head="recurrent",
+                    A=d["A"], c=d["c"], h0=d["h0"])
+    last_in = o["tokens"][:, -2]
+    assert np.array_equal(o["state"], tanh_p(d["E"][last_in]))
+    d["E"][:] = 0
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head="recurrent",
+                    A=d["A"], c=d["c"], h0=d["h0"])
+    assert np.array_equal(o["state"], np.broadcast_to(tanh_p(d["c"]), (2, 8)))
+
+
+@pytest.mark.parametrize("head", ["markov", "recurrent"])
+def test_resume_invariance(head):
+    d = datagen.make_inputs(500, 32, 2, 16, head=head, seed=16)
+    kw = dict(s_w=d["s_w"], head=head, A=d["A"], c=d["c"], temperature=1, seed=99)
+    full = oracle.walk(d["W"], d["E"], d["base"], d["x0"], h0=d["h0"], **kw)
+    a = oracle.walk(d["W"], d["E"], d["base"][:, :7], d["x0"], h0=d["h0"], **kw)
+    b = oracle.walk(d["W"], d["E"], d["base"][:, 7:], a["tokens"][:, -1], h0=a["state"],
+                    step_offset=7, **kw)
+    assert np.array_equal(np.concatenate([a["tokens"], b["tokens"]], 1), full["tokens"])
+    assert np.array_equal(np.concatenate([a["logits"], b["logits"]], 1), full["logits"])
+
+
+def test_batch_rows_independent():
+    d = datagen.make_inputs(400, 32, 3, 5, seed=17)
+    full = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], temperature=1, seed=5)
+    for b in range(3):
+        one = oracle.walk(d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"])
+        g = oracle.walk(d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"])
+        assert np.array_equal(one["tokens"], g["tokens"])
+    # T=1 noise is keyed by the batch index, so row b of a batch differs from a lone row 0
+    lone = oracle.walk(d["W"], d["E"], d["base"][2:3], d["x0"][2:3], s_w=d["s_w"], temperature=1, seed=5)
+    assert lone["tokens"].shape == (1, 5) and full["tokens"].shape == (3, 5)
+
+
+def test_project_bf16_exact_sum():
+    rng = np.random.default_rng(18)
+    W = bf16_rne(rng.standard_t(4, (20, 64)).astype(np.float32))
+    u = bf16_rne(rng.normal(0, 0.1, 64).astype(np.float32))
+    p = oracle.project_bf16(bf16_to_f32(W).astype(np.float64), u)
+    Wf, uf = bf16_to_f32(W), bf16_to_f32(u)
+    for v in range(20):
+        s = sum(_F(Wf[v, k]) * _F(uf[k]) for k in range(64))
+        assert Fraction(float(p[v])) == rnd32(s)
+
+
+def test_bf16_walk_bruteforce_small():
+    d = datagen.make_inputs(16, 8, 1, 3, wtype="bf16", seed=19)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], wtype="bf16", keep_z=True)
+    Wf = bf16_to_f32(d["W"])
+    x = int(d["x0"][0])
+    for t in range(3):
+        u = bf16_to_f32(bf16_rne(d["E"][x]))
+        sc = []
+        for v in range(16):
+            z = rnd32(rnd32(sum(_F(Wf[v, k]) * _F(u[k]) for k in range(8))) + _F(bf16_to_f32(d["base"][0, t, v])))
+            assert Fraction(float(o["z"][0, t, v])) == z
+            sc.append((-rnd_bf16(z), v))
+        x = min(sc)[1]
+        assert o["tokens"][0, t] == x
