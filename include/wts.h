@@ -1,0 +1,142 @@
+/*
+ * wts.h -- C ABI of the walk-resident serial draft head library (gfx950).
+ *
+ * The operation: "Weights That Stay: On-Chip Megakernels for Serial Heads in
+ * Speculative Decoding" (arXiv 2611.00506).  A serial draft head walks gamma
+ * steps; each step projects a rank-r state through the same immutable V x r
+ * vocabulary matrix W, adds base logits, selects one token over the whole
+ * vocabulary and advances the state (abstract; Fig. 2).  The library runs
+ * the whole walk in one persistent kernel that keeps each compute unit's
+ * shard of W on chip (Fig. 1), selects tokens on the GPU across workgroups
+ * (Fig. 8) and advances the state in the kernel; it also runs the same walk
+ * one launch per step, streaming W every step, for comparison (Fig. 4,
+ * Fig. 11).
+ *
+ * Conventions for every entry point:
+ *   - "device pointer" = memory of the GPU selected by `device` (e.g. a torch
+ *     tensor's data_ptr()).  The library never frees caller memory.
+ *   - Every call returns a wts_status and never aborts or throws.  Errors the
+ *     host can see are returned before anything is enqueued; outputs are then
+ *     untouched.  Errors only the device can see (x0 out of range, barrier
+ *     watchdog) are latched in the context and read with wts_get_error().
+ *   - Calls on one context must not overlap (one walk in flight per context
+ *     on one stream at a time; use one context per concurrent stream).
+ */
+#ifndef WTS_H_
+#define WTS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wts_status {
+  WTS_OK = 0,
+  WTS_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, size out of range      */
+  WTS_ERR_UNSUPPORTED = 2,   /* valid but not built (e.g. r != 256)             */
+  WTS_ERR_NO_MEMORY = 3,     /* device allocation failed                        */
+  WTS_ERR_DEVICE = 4,        /* HIP runtime / launch / cooperative-launch error */
+  WTS_ERR_TIMEOUT = 5,       /* device watchdog expired in the grid barrier     */
+  WTS_ERR_TOKEN_RANGE = 6    /* an x0 entry was outside [0, V)                  */
+} wts_status;
+
+/* Head kinds (Fig. 13): Markov u_t = E[x_{t-1}];
+ * recurrent h_t = tanh(A h_{t-1} + E[x_{t-1}] + c). */
+enum { WTS_HEAD_MARKOV = 0, WTS_HEAD_RECURRENT = 1 };
+
+/* Storage of W (Fig. 1: int8 with per-row scales, or bf16). */
+enum { WTS_W_INT8 = 0, WTS_W_BF16 = 1 };
+
+/* Execution of a walk.
+ *  RESIDENT: one persistent launch; each workgroup keeps its W shard on chip
+ *            (registers, then LDS) and streams only what does not fit.
+ *  STREAM:   one persistent launch that re-reads every W tile from memory at
+ *            every step (whole-walk fusion without residency, Fig. 4/11).
+ *  STEPWISE: one launch per step, W streamed every step; the kernel boundary
+ *            replaces the grid barrier.
+ * All three compute identical tokens and logits. */
+enum { WTS_EXEC_RESIDENT = 0, WTS_EXEC_STREAM = 1, WTS_EXEC_STEPWISE = 2 };
+
+typedef struct wts_ctx wts_ctx;
+
+typedef struct wts_create_params {
+  int32_t V;              /* vocabulary rows, 1 <= V <= 262143                 */
+  int32_t r;              /* rank; only 256 is built                           */
+  int32_t head;           /* WTS_HEAD_*                                        */
+  int32_t wtype;          /* WTS_W_*                                           */
+  const void* W;          /* device, [V][r] row-major: int8, or bf16 bits      */
+  const float* w_scale;   /* device, [V] fp32 per-row scale (int8 only)        */
+  const float* E;         /* device, [V][r] fp32 embedding rows                */
+  const uint16_t* A;      /* device, [r][r] bf16 bits (recurrent only)         */
+  const float* c;         /* device, [r] fp32 (recurrent only)                 */
+  int32_t max_batch;      /* 1..16                                             */
+  int32_t max_steps;      /* 1..64                                             */
+  int32_t resident_tiles; /* -1: planner's choice.  Otherwise the number of
+                             16-row tiles each wave keeps in registers (0..the
+                             built maximum); the rest is streamed.            */
+  int32_t lds_tiles;      /* -1: planner's choice.  Otherwise 16-row tiles per
+                             wave kept in LDS (after the register tiles).     */
+  int32_t device;         /* HIP device ordinal                                */
+} wts_create_params;
+
+typedef struct wts_walk_params {
+  int32_t B;              /* batch rows, 1..max_batch                          */
+  int32_t gamma;          /* steps, 1..max_steps                               */
+  int32_t step_offset;    /* step index of t=0 in the noise key (resume)       */
+  int32_t temperature;    /* 0 greedy, 1 Gumbel-max; anything else invalid    */
+  uint64_t seed;          /* noise key (T=1)                                   */
+  const uint16_t* base;   /* device, [B][gamma][V] bf16 bits                   */
+  const int32_t* x0;      /* device, [B] tokens before step 0                  */
+  const float* h0;        /* device, [B][r] fp32 initial state (recurrent)     */
+  int32_t* tokens_out;    /* device, [B][gamma] int32 (required)               */
+  uint16_t* logits_out;   /* device, [B][gamma][V] bf16 bits, or NULL          */
+  float* state_out;       /* device, [B][r] fp32 final state, or NULL          */
+  int32_t exec;           /* WTS_EXEC_*                                        */
+  int32_t reserved;       /* must be 0                                         */
+  void* stream;           /* hipStream_t (NULL = default stream)               */
+} wts_walk_params;
+
+typedef struct wts_plan {
+  int32_t grid;            /* workgroups of the persistent kernel (= CUs)      */
+  int32_t waves;           /* waves per workgroup                              */
+  int32_t tiles;           /* 16-row tiles of W (ceil(V/16))                   */
+  int32_t tiles_per_wave;  /* most tiles any wave owns                         */
+  int32_t reg_tiles;       /* per wave, held in registers                      */
+  int32_t lds_tiles;       /* per wave, held in LDS                            */
+  int32_t stream_tiles;    /* per wave (max), streamed each step               */
+  int64_t resident_bytes;  /* W bytes on chip over the whole GPU               */
+  int64_t streamed_bytes;  /* W bytes read from memory per step                */
+  int64_t w_bytes;         /* V * r * element size                             */
+} wts_plan;
+
+/* Create a head: validates, plans residency, and copies W into a tile-major
+ * layout owned by the context (plus the quantised embedding rows, Fig. 7).
+ * Borrows E, A, c: keep them alive until wts_destroy.  Synchronous. */
+wts_status wts_create(const wts_create_params* p, wts_ctx** out);
+
+/* Enqueue one walk on p->stream (asynchronous; inputs must stay alive and
+ * unmodified until the stream reaches the walk's end).  Writes tokens_out
+ * [b][t] = token chosen at step t, and optionally logits_out and state_out. */
+wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p);
+
+/* Synchronizes the device, then frees everything the context owns.
+ * NULL is ignored. */
+void wts_destroy(wts_ctx* ctx);
+
+/* Synchronizes the device and returns the error latched by walks since the
+ * last clear (WTS_OK if none).  clear != 0 resets the latch. */
+wts_status wts_get_error(wts_ctx* ctx, int clear);
+
+/* Residency a walk of B batch rows under `exec` uses (B selects the batch
+ * bucket 1, 2, 4, 8 or 16; larger buckets keep fewer tiles in registers). */
+wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, wts_plan* out);
+
+/* Static description of a status code. */
+const char* wts_status_string(wts_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WTS_H_ */

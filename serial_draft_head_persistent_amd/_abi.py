@@ -1,0 +1,82 @@
+"""ctypes declarations of the C ABI in include/wts.h (argument marshalling only).
+
+Every computation happens in libwts.so (HIP, gfx950).  Importing this module
+loads the library and raises ImportError if it has not been built; there is
+no fallback path.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwts.so")
+
+WTS_OK = 0
+STATUS_NAMES = {0: "WTS_OK", 1: "WTS_ERR_INVALID_ARG", 2: "WTS_ERR_UNSUPPORTED", 3: "WTS_ERR_NO_MEMORY",
+                4: "WTS_ERR_DEVICE", 5: "WTS_ERR_TIMEOUT", 6: "WTS_ERR_TOKEN_RANGE"}
+HEAD = {"markov": 0, "recurrent": 1}
+WTYPE = {"int8": 0, "bf16": 1}
+EXEC = {"resident": 0, "stream": 1, "stepwise": 2}
+
+EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string"]
+
+c_int32, c_uint64, c_void_p = ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
+
+
+class CreateParams(ctypes.Structure):
+    _fields_ = [("V", c_int32), ("r", c_int32), ("head", c_int32), ("wtype", c_int32),
+                ("W", c_void_p), ("w_scale", c_void_p), ("E", c_void_p), ("A", c_void_p), ("c", c_void_p),
+                ("max_batch", c_int32), ("max_steps", c_int32), ("resident_tiles", c_int32),
+                ("lds_tiles", c_int32), ("device", c_int32)]
+
+
+class WalkParams(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("gamma", c_int32), ("step_offset", c_int32), ("temperature", c_int32),
+                ("seed", c_uint64), ("base", c_void_p), ("x0", c_void_p), ("h0", c_void_p),
+                ("tokens_out", c_void_p), ("logits_out", c_void_p), ("state_out", c_void_p),
+                ("exec", c_int32), ("reserved", c_int32), ("stream", c_void_p)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("grid", c_int32), ("waves", c_int32), ("tiles", c_int32), ("tiles_per_wave", c_int32),
+                ("reg_tiles", c_int32), ("lds_tiles", c_int32), ("stream_tiles", c_int32),
+                ("resident_bytes", ctypes.c_int64), ("streamed_bytes", ctypes.c_int64),
+                ("w_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class WtsError(RuntimeError):
+    def __init__(self, code, what=""):
+        self.code = code
+        super().__init__(f"{what}: {STATUS_NAMES.get(code, code)}")
+
+
+def load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run python -m serial_draft_head_persistent_amd.build")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.wts_create.argtypes = [P(CreateParams), P(c_void_p)]
+    lib.wts_create.restype = ctypes.c_int
+    lib.wts_walk.argtypes = [c_void_p, P(WalkParams)]
+    lib.wts_walk.restype = ctypes.c_int
+    lib.wts_destroy.argtypes = [c_void_p]
+    lib.wts_destroy.restype = None
+    lib.wts_get_error.argtypes = [c_void_p, ctypes.c_int]
+    lib.wts_get_error.restype = ctypes.c_int
+    lib.wts_get_plan.argtypes = [c_void_p, c_int32, c_int32, P(Plan)]
+    lib.wts_get_plan.restype = ctypes.c_int
+    lib.wts_status_string.argtypes = [ctypes.c_int]
+    lib.wts_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib

@@ -1,0 +1,91 @@
+// Internal declarations shared by the host runtime and the gfx950 kernels of
+// the walk-resident serial draft head ("Weights That Stay", arXiv 2611.00506).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wts {
+
+constexpr int kR = 256;           // latent rank the kernels are built for
+constexpr int kTileRows = 16;     // vocabulary rows per W tile (one MFMA N block)
+constexpr int kWaves = 8;         // waves per workgroup of the persistent kernel
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxB = 16;
+constexpr int kMaxSteps = 64;
+// 16-row W tiles a wave of the persistent kernel holds in VGPRs.  Larger
+// batches need more registers for latents and keys, so they keep fewer tiles
+// in registers and more in LDS.
+constexpr int reg_tiles_max(int wtype, int BB) {
+  return wtype == 0 ? (BB >= 8 ? 3 : 5) : 2;
+}
+constexpr int kChunksI8 = 4;      // 16-byte lane chunks per int8 tile (64 k each)
+constexpr int kChunksBF = 8;      // 16-byte lane chunks per bf16 tile (32 k each)
+constexpr int kTileBytesI8 = kTileRows * kR;       // 4 KiB
+constexpr int kTileBytesBF = kTileRows * kR * 2;   // 8 KiB
+// LDS of the persistent kernel: scratch for reductions and the latent, then
+// W tiles.  Asking for more than half of the 160 KiB also pins one workgroup
+// per compute unit.
+constexpr int kLdsScratch = 16384;
+constexpr int kLdsMax = 163840;
+
+constexpr int kHeadMarkov = 0;
+constexpr int kHeadRecurrent = 1;
+
+// Device control block of one context.  Zeroed at create; afterwards each
+// walk (parity k & 1) clears the slots and counter of the next walk (parity
+// (k + 1) & 1) before it touches its own, so no host-side reset is needed.
+struct Ctrl {
+  unsigned long long slot[2][kMaxSteps][kMaxB];  // per walk parity: max keys
+  unsigned int arrive[2];                        // per walk parity: arrivals
+  unsigned int err;                              // latched wts_status
+  unsigned int pad[61];
+};
+
+struct WalkArgs {
+  // from the context
+  const int4* Wp;          // tile-major W: [tiles][chunks][64 lanes] x 16 B
+  const float* sw;         // [tiles * 16] per-row scale (int8), 0 on pad rows
+  const int8_t* Eq;        // [V][512]: hi[256] | lo[256] of each E row (int8)
+  const float* Es;         // [V] s_hi of each E row (int8 Markov)
+  const uint16_t* Eb;      // [V][256] bf16 E rows (bf16 Markov)
+  const float* E;          // [V][256] fp32 (recurrent)
+  const uint16_t* A;       // [256][256] bf16 (recurrent)
+  const float* c;          // [256] (recurrent)
+  Ctrl* ctrl;
+  int V;
+  int tiles;
+  int head;
+  int reg_tiles;           // per wave, in registers
+  int lds_tiles;           // per wave, in LDS
+  // of this walk
+  int B;
+  int gamma;
+  int step_offset;
+  int temperature;
+  unsigned seed_lo;
+  unsigned seed_hi;
+  int parity;
+  int step;                // step-wise launches: the step this launch runs
+  const uint16_t* base;
+  const int* x0;
+  const float* h0;
+  int* tokens;
+  uint16_t* logits;
+  float* state;
+  long long timeout_ticks; // watchdog, in s_memrealtime ticks (100 MHz)
+};
+
+// Launchers (wts_kernels.hip).  Each returns the HIP error of its launch.
+hipError_t launch_repack_i8(const int8_t* W, const float* w_scale, int V, int tiles,
+                            int4* Wp, float* sw, hipStream_t s);
+hipError_t launch_repack_bf16(const uint16_t* W, int V, int tiles, int4* Wp, hipStream_t s);
+hipError_t launch_quant_rows(const float* E, int V, int8_t* Eq, float* Es, hipStream_t s);
+hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s);
+hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes,
+                       hipStream_t s);
+hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s);
+hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
+hipError_t prepare_kernels(int lds_bytes);
+
+}  // namespace wts

@@ -1,0 +1,928 @@
+// gfx950 kernels of the walk-resident serial draft head.
+//
+// Method: "Weights That Stay: On-Chip Megakernels for Serial Heads in
+// Speculative Decoding" (arXiv 2611.00506).  One persistent launch runs the
+// whole gamma-step walk (Fig. 1, Fig. 4): each workgroup keeps its shard of
+// the vocabulary projection W on chip, projects the step's latent through it,
+// selects a local winner, and all workgroups agree on the common winner
+// through a 64-bit atomic maximum plus an arrival count (Fig. 8) before the
+// state advances in the kernel.  int8 W uses the two-int8-vector latent of
+// Fig. 7; bf16 W uses the latent rounded to bf16.
+//
+// MI355X mapping (not the pages' H100/B200 design):
+//  * one workgroup of 8 waves per CU; a wave owns every 8th 16-row tile of
+//    its workgroup's contiguous tile range;
+//  * a tile is one MFMA N block: the latent rows are the A operand (16 x K),
+//    the 16 vocabulary rows of the tile the B operand (K x 16), so the
+//    projection of a step is a chain of v_mfma_i32_16x16x64_i8 (int8 W) or
+//    v_mfma_f32_16x16x32_bf16 (bf16 W) per tile;
+//  * when the batch leaves latent rows unused, several tiles share one MFMA
+//    accumulator by placing the latent in different A rows ("slots"), so all
+//    64 lanes of the result carry useful logits;
+//  * W tiles live in VGPRs (registers), then LDS, and the remainder streams
+//    from HBM each step with one tile of prefetch;
+//  * the grid barrier is a device-scope atomic max on a per-step slot, an
+//    arrival counter with release order, and one spinning lane per
+//    workgroup with s_sleep back-off and a wall-clock watchdog.
+//
+// Bit-exactness with the host reference needs: no contraction of a*b+c
+// (built with -ffp-contract=off), IEEE division (default), rintf half-even.
+
+#include "wts_internal.h"
+
+namespace wts {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ----------------------------------------------------------------------------
+// scalar helpers
+// ----------------------------------------------------------------------------
+
+// bf16 = upper half of binary32, rounded to nearest even (Fig. 7: "rounded
+// once to bf16").
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t b = __float_as_uint(x);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+__device__ __forceinline__ float bf16_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Selection key (Fig. 8, "packs its local winner"): the high word orders
+// binary32 scores (-0 folded into +0), the low word is 0xFFFFFFFF - v so the
+// lowest index wins among equal scores.  0 is below every key.
+__device__ __forceinline__ unsigned long long sel_key(float s, int v) {
+  uint32_t b = __float_as_uint(s);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+}
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+// Portable elementary functions, one binary32 operation at a time.
+// log: x = m 2^e, m in [sqrt(1/2), sqrt(2)); log m = 2 atanh(s), s = (m-1)/(m+1),
+// series through s^9; ln 2 split in a high part exact for |e| <= 256 and a
+// low part (Cody-Waite).
+constexpr float kLn2Hi = 0.693145751953125f;
+constexpr float kLn2Lo = (float)(0.69314718055994530942 - 0.693145751953125);
+constexpr float kInvLn2 = (float)(1.0 / 0.69314718055994530942);
+constexpr float kLogC9 = (float)(1.0 / 9.0);
+constexpr float kLogC7 = (float)(1.0 / 7.0);
+constexpr float kLogC5 = (float)(1.0 / 5.0);
+constexpr float kLogC3 = (float)(1.0 / 3.0);
+
+__device__ float log_p(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  int e = (int)((bits >> 23) & 0xFFu) - 126;
+  float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F000000u);
+  if (m < 0.70710677f) {
+    m = m * 2.0f;
+    e = e - 1;
+  }
+  const float f = m - 1.0f;
+  const float s = f / (2.0f + f);
+  const float z = s * s;
+  float p = kLogC9 * z;
+  p = (p + kLogC7) * z;
+  p = (p + kLogC5) * z;
+  p = (p + kLogC3) * z;
+  const float lm = 2.0f * (s + s * p);
+  const float ef = (float)e;
+  return ef * kLn2Hi + (ef * kLn2Lo + lm);
+}
+
+// e^y for y in [-20, 0]: n = rint(y / ln 2), reduced argument, degree-8
+// Taylor polynomial (Horner), exact scaling by 2^n.
+__device__ float exp_p(float y) {
+  const float n = rintf(y * kInvLn2);
+  const float f = (y - n * kLn2Hi) - n * kLn2Lo;
+  float p = (float)(1.0 / 40320.0);
+  p = p * f + (float)(1.0 / 5040.0);
+  p = p * f + (float)(1.0 / 720.0);
+  p = p * f + (float)(1.0 / 120.0);
+  p = p * f + (float)(1.0 / 24.0);
+  p = p * f + (float)(1.0 / 6.0);
+  p = p * f + 0.5f;
+  p = p * f + 1.0f;
+  p = p * f + 1.0f;
+  const float scale = __uint_as_float((uint32_t)((int)n + 127) << 23);
+  return p * scale;
+}
+
+// tanh: odd Taylor series below 1/4, (1 - e^{-2a}) / (1 + e^{-2a}) up to 10,
+// 1 beyond; sign of x restored.
+__device__ float tanh_p(float x) {
+  const float a = fabsf(x);
+  if (a < 0.25f) {
+    const float x2 = x * x;
+    float t = (float)(-1382.0 / 155925.0);
+    t = t * x2 + (float)(62.0 / 2835.0);
+    t = t * x2 + (float)(-17.0 / 315.0);
+    t = t * x2 + (float)(2.0 / 15.0);
+    t = t * x2 + (float)(-1.0 / 3.0);
+    return x + x * (x2 * t);
+  }
+  float r = 1.0f;
+  if (a < 10.0f) {
+    const float q = exp_p(-2.0f * a);
+    r = (1.0f - q) / (1.0f + q);
+  }
+  return x < 0.0f ? -r : r;
+}
+
+// Philox4x32-10 (Salmon et al., SC'11): 10 rounds of two 32x32->64 products,
+// Weyl key schedule between rounds.  Noise for (b, step, v): counter
+// (v >> 2, step, b, 0), key (seed_lo, seed_hi), output word v & 3.
+__device__ float gumbel(uint32_t k0, uint32_t k1, int b, int step, int v) {
+  uint32_t c0 = (uint32_t)v >> 2, c1 = (uint32_t)step, c2 = (uint32_t)b, c3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  const int sel = v & 3;
+  const uint32_t w = sel == 0 ? c0 : sel == 1 ? c1 : sel == 2 ? c2 : c3;
+  // U = (2 (w >> 9) + 1) 2^-24, exact, in (0, 1)
+  const float u = (float)(2u * (w >> 9) + 1u) * 5.9604644775390625e-08f;
+  const float y = -log_p(u);
+  return -log_p(y);
+}
+
+// ----------------------------------------------------------------------------
+// create-time kernels
+// ----------------------------------------------------------------------------
+
+// W [V][256] int8 -> tile-major [tile][chunk c<4][lane] x 16 B, where lane
+// l carries row 16*tile + (l & 15), columns 64c + 16(l >> 4) .. +16 -- the B
+// operand of v_mfma_i32_16x16x64_i8 for that chunk.  Pad rows are zero.
+__global__ void repack_i8_kernel(const int8_t* __restrict__ W, const float* __restrict__ ws,
+                                 int V, int tiles, int4* __restrict__ Wp, float* __restrict__ sw) {
+  const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)tiles * kChunksI8 * 64;
+  if (id >= total) return;
+  const int lane = (int)(id & 63);
+  const int c = (int)((id >> 6) % kChunksI8);
+  const int tile = (int)(id / (64 * kChunksI8));
+  const int row = tile * kTileRows + (lane & 15);
+  int4 v = make_int4(0, 0, 0, 0);
+  if (row < V) v = *(const int4*)(W + (size_t)row * kR + c * 64 + (lane >> 4) * 16);
+  Wp[id] = v;
+  if (c == 0 && lane < 16) sw[tile * kTileRows + lane] = row < V ? ws[row] : 0.0f;
+}
+
+// W [V][256] bf16 -> [tile][chunk c<8][lane] x 16 B: row 16*tile + (l & 15),
+// columns 32c + 8(l >> 4) .. +8 (B operand of v_mfma_f32_16x16x32_bf16).
+__global__ void repack_bf16_kernel(const uint16_t* __restrict__ W, int V, int tiles,
+                                   int4* __restrict__ Wp) {
+  const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)tiles * kChunksBF * 64;
+  if (id >= total) return;
+  const int lane = (int)(id & 63);
+  const int c = (int)((id >> 6) % kChunksBF);
+  const int tile = (int)(id / (64 * kChunksBF));
+  const int row = tile * kTileRows + (lane & 15);
+  int4 v = make_int4(0, 0, 0, 0);
+  if (row < V) v = *(const int4*)(W + (size_t)row * kR + c * 32 + (lane >> 4) * 8);
+  Wp[id] = v;
+}
+
+// Wave-wide maximum of a float (all lanes get the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// Two-int8-vector latent of one 256-vector held 4 values per lane (Fig. 7):
+// symmetric absmax scale s_hi = amax/127, hi = rint(u 127/amax), residual
+// r = u - s_hi hi, lo = rint(r 256 * 127/amax), both clamped to +-127,
+// s_lo = s_hi / 256.  Returns s_hi; hi/lo of elements 4*lane..+3 in *hi,*lo.
+__device__ __forceinline__ float quant4(const float u[4], uint32_t* hi4, uint32_t* lo4) {
+  float amax = fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3])));
+  amax = wave_max(amax);
+  uint32_t ph = 0, pl = 0;
+  float s_hi = 0.0f;
+  if (amax != 0.0f) {
+    s_hi = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    const float inv256 = inv * 256.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float h = rintf(u[i] * inv);
+      h = fminf(fmaxf(h, -127.0f), 127.0f);
+      const float res = u[i] - s_hi * h;
+      float l = rintf(res * inv256);
+      l = fminf(fmaxf(l, -127.0f), 127.0f);
+      ph |= ((uint32_t)(int)h & 0xFFu) << (8 * i);
+      pl |= ((uint32_t)(int)l & 0xFFu) << (8 * i);
+    }
+  }
+  *hi4 = ph;
+  *lo4 = pl;
+  return s_hi;
+}
+
+// E [V][256] fp32 -> Eq [V][512] (hi | lo) and Es [V] (s_hi).  One wave per row.
+__global__ void quant_rows_kernel(const float* __restrict__ E, int V, int8_t* __restrict__ Eq,
+                                  float* __restrict__ Es) {
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= V) return;  // whole wave leaves together
+  const float4 u4 = *(const float4*)(E + (size_t)row * kR + lane * 4);
+  const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+  uint32_t h, l;
+  const float s = quant4(u, &h, &l);
+  *(uint32_t*)(Eq + (size_t)row * 512 + lane * 4) = h;
+  *(uint32_t*)(Eq + (size_t)row * 512 + 256 + lane * 4) = l;
+  if (lane == 0) Es[row] = s;
+}
+
+// E [V][256] fp32 -> bf16 rows.
+__global__ void bf16_rows_kernel(const float* __restrict__ E, long long n, uint16_t* __restrict__ Eb) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) Eb[i] = (uint16_t)bf16_rne(E[i]);
+}
+
+// ----------------------------------------------------------------------------
+// the walk
+// ----------------------------------------------------------------------------
+
+// Geometry of one (W type, batch bucket).  The A operand carries LPB latent
+// rows per batch row (hi and lo for int8, one for bf16).  With RPS latent
+// rows per slot, S = 16 / RPS tiles share one accumulator.
+template <int WT, int BB>
+struct Geo {
+  static constexpr int LPB = WT == 0 ? 2 : 1;
+  static constexpr int ROWS = LPB * BB;
+  static constexpr int NM = ROWS > 16 ? ROWS / 16 : 1;
+  static constexpr int RPS = WT == 0 ? (ROWS <= 4 ? 4 : (ROWS <= 8 ? 8 : 16)) : 16;
+  static constexpr int S = 16 / RPS;
+  static constexpr int CH = WT == 0 ? kChunksI8 : kChunksBF;
+  static constexpr int RT = reg_tiles_max(WT, BB);
+  static constexpr int NG = (RT + S - 1) / S;
+  static constexpr int NE = 4 / LPB;  // batch entries per lane and M block
+};
+
+// LDS map of the persistent and step kernels.
+constexpr int kOffRed = 0;                       // u64 [kWaves][kMaxB]
+constexpr int kOffX = kOffRed + 8 * kWaves * kMaxB;   // int [kMaxB]
+constexpr int kOffShi = kOffX + 4 * kMaxB;        // float [kMaxB]
+constexpr int kOffFlag = kOffShi + 4 * kMaxB;     // int
+constexpr int kOffLat = 2048;                     // int8 [kMaxB][2][256] or bf16 [kMaxB][256]
+constexpr int kOffH = kOffLat + kMaxB * 512;       // float [kMaxB][256]
+constexpr int kScratchMarkov = 2048;
+constexpr int kScratchRec = kOffH + kMaxB * kR * 4;  // 26624
+constexpr int kOffAt = 32768;                      // recurrent: A^T bf16 [256][256]
+
+
+__device__ __forceinline__ v4i mma(const v4i& a, const v4i& b, const v4i& c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mma(const v4i& a, const v4i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+template <int WT> struct AccT { typedef v4i T; };
+template <> struct AccT<1> { typedef v4f T; };
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long k, int m) {
+  const unsigned lo = __shfl_xor((unsigned)k, m, 64);
+  const unsigned hi = __shfl_xor((unsigned)(k >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Per-lane roles.  The MFMA result puts latent row 4q + j (q = lane / 16,
+// j = 0..3) of vocabulary column n = lane % 16 in register j.  A lane's
+// A-operand row is n.
+template <int WT, int BB>
+struct Roles {
+  using Gm = Geo<WT, BB>;
+  int lane, n, q, aslot, aw, cslot, cw0;
+  __device__ __forceinline__ explicit Roles(int l) {
+    lane = l;
+    n = l & 15;
+    q = l >> 4;
+    aslot = n / Gm::RPS;
+    aw = n % Gm::RPS;
+    cslot = (4 * q) / Gm::RPS;
+    cw0 = (4 * q) % Gm::RPS;
+  }
+  // batch row of result entry e of M block m (int8: registers 2e (hi), 2e+1 (lo))
+  __device__ __forceinline__ int bent(int m, int e) const {
+    return WT == 0 ? (m * Gm::RPS + cw0) / 2 + e : m * Gm::RPS + cw0 + e;
+  }
+  // batch row and hi/lo half of this lane's A-operand row in M block m
+  __device__ __forceinline__ int arow_b(int m) const { return (m * Gm::RPS + aw) / Gm::LPB; }
+  __device__ __forceinline__ int arow_hl(int m) const { return (m * Gm::RPS + aw) % Gm::LPB; }
+};
+
+// Latent of this step as MFMA A operands: slot s holds the latent rows in A
+// rows [s*RPS, (s+1)*RPS) and zeros elsewhere.
+template <int WT, int BB, int HEAD>
+__device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, BB>& ro, const int* sx,
+                                            const char* lds, v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH]) {
+  using Gm = Geo<WT, BB>;
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m) {
+    const int b = ro.arow_b(m);
+    const bool ok = b < a.B;
+    const int hl = ro.arow_hl(m);
+    v4i d[Gm::CH];
+    if (HEAD == kHeadMarkov) {
+      const int x = ok ? sx[b] : 0;
+      const v4i* src = WT == 0 ? (const v4i*)(a.Eq + (size_t)x * 512 + hl * 256 + ro.q * 16)
+                               : (const v4i*)(a.Eb + (size_t)x * kR + ro.q * 8);
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) d[c] = ok ? src[c * 4] : v4i{0, 0, 0, 0};
+    } else {
+      const char* src = WT == 0 ? lds + kOffLat + (b * 2 + hl) * 256 + ro.q * 16
+                                : lds + kOffLat + (b * kR + ro.q * 8) * 2;
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) d[c] = ok ? *(const v4i*)(src + c * 64) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < Gm::S; ++s)
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = (ro.aslot == s) ? d[c] : v4i{0, 0, 0, 0};
+  }
+}
+
+// Fig. 7 epilogue for the result entries of one M block, then the local
+// selection (Fig. 8 step 1): logit = bf16(((acc_hi s_hi + acc_lo s_lo) s_w) +
+// base) for int8 W, bf16(acc + base) for bf16 W; score = logit (T=0) or
+// logit + Gumbel noise (T=1); keep the largest key per batch entry.
+template <int WT, int BB, int TEMP>
+__device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
+                                         const typename AccT<WT>::T& acc, int v, bool ok, float sw,
+                                         const uint32_t (&bv)[Geo<WT, BB>::NE],
+                                         const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                         unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+  using Gm = Geo<WT, BB>;
+#pragma unroll
+  for (int e = 0; e < Gm::NE; ++e) {
+    const int b = ro.bent(m, e);
+    if (ok && b < a.B) {
+      float z;
+      if (WT == 0) {
+        const float zh = (float)acc[2 * e] * shi[m][e];
+        const float zl = (float)acc[2 * e + 1] * (shi[m][e] * 0.00390625f);
+        z = zh + zl;
+        z = z * sw;
+      } else {
+        z = acc[e];
+      }
+      z = z + bf16_f32(bv[e]);
+      const uint32_t lg = bf16_rne(z);
+      if (a.logits) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
+      float sc = bf16_f32(lg);
+      if (TEMP) sc = sc + gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
+      best[m][e] = umax64(best[m][e], sel_key(sc, v));
+    }
+  }
+}
+
+// Base logits of one result entry set (bf16 bits), zero where unused.
+template <int WT, int BB>
+__device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
+                                          int v, bool ok, uint32_t (&bv)[Geo<WT, BB>::NE]) {
+  using Gm = Geo<WT, BB>;
+#pragma unroll
+  for (int e = 0; e < Gm::NE; ++e) {
+    const int b = ro.bent(m, e);
+    bv[e] = (ok && b < a.B) ? (uint32_t)a.base[((size_t)b * a.gamma + t) * a.V + v] : 0u;
+  }
+}
+
+// Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), read from LDS
+// for i < i0 + nlds and from memory otherwise, with one tile of prefetch.
+template <int WT, int BB, int TEMP, int NWV>
+__device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
+                                             int w, int i0, int nlds, int nw, const char* ldsw,
+                                             const v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH],
+                                             const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                             unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+  using Gm = Geo<WT, BB>;
+  using AT = typename AccT<WT>::T;
+  constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
+  if (i0 >= nw) return;
+  v4i cur[Gm::CH];
+  float csw = 0.0f;
+  uint32_t cbv[Gm::NM][Gm::NE];
+  auto fetch = [&](int i, v4i (&dst)[Gm::CH], float& dsw, uint32_t (&dbv)[Gm::NM][Gm::NE]) {
+    const int tile = tb + w + NWV * i;
+    if (i < i0 + nlds) {
+      const char* p = ldsw + (size_t)(i - i0) * TB + ro.lane * 16;
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) dst[c] = *(const v4i*)(p + c * 1024);
+    } else {
+      const v4i* p = (const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane;
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) dst[c] = p[c * 64];
+    }
+    const int v = tile * kTileRows + ro.n;
+    const bool ok = ro.cslot == 0 && v < a.V;
+    dsw = (WT == 0 && ok) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
+#pragma unroll
+    for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, dbv[m]);
+  };
+  fetch(i0, cur, csw, cbv);
+  for (int i = i0; i < nw; ++i) {
+    v4i nxt[Gm::CH];
+    float nsw = 0.0f;
+    uint32_t nbv[Gm::NM][Gm::NE];
+    if (i + 1 < nw) fetch(i + 1, nxt, nsw, nbv);
+    const int tile = tb + w + NWV * i;
+    const int v = tile * kTileRows + ro.n;
+    const bool ok = ro.cslot == 0 && v < a.V;
+#pragma unroll
+    for (int m = 0; m < Gm::NM; ++m) {
+      AT acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][0][c], cur[c], acc);
+      epilogue<WT, BB, TEMP>(a, ro, t, m, acc, v, ok, csw, cbv[m], shi, best);
+    }
+    if (i + 1 < nw) {
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) cur[c] = nxt[c];
+      csw = nsw;
+#pragma unroll
+      for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+        for (int e = 0; e < Gm::NE; ++e) cbv[m][e] = nbv[m][e];
+    }
+  }
+}
+
+// Wave reduction of the keys of lanes that hold the same batch rows, then
+// one representative lane per batch row writes red[w][b].
+template <int WT, int BB>
+__device__ __forceinline__ void reduce_to_lds(const WalkArgs& a, const Roles<WT, BB>& ro, int w,
+                                              unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                              unsigned long long* red) {
+  using Gm = Geo<WT, BB>;
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+    for (int e = 0; e < Gm::NE; ++e) {
+      unsigned long long k = best[m][e];
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) k = umax64(k, shfl_xor_u64(k, s));
+      if (Gm::RPS == 4) {
+        k = umax64(k, shfl_xor_u64(k, 16));
+        k = umax64(k, shfl_xor_u64(k, 32));
+      } else if (Gm::RPS == 8) {
+        k = umax64(k, shfl_xor_u64(k, 32));
+      }
+      const int b = ro.bent(m, e);
+      if (ro.n == 0 && ro.q < Gm::RPS / 4 && b < a.B) red[w * kMaxB + b] = k;
+    }
+}
+
+__device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
+  atomicCAS(&ctrl->err, 0u, code);
+}
+
+// Recurrent head, first half of a step (Fig. 13): h_{t+1} = tanh(A h_t +
+// E[x_t] + c) with the A h_t sums (ascending k) already in acc; then the
+// latent rows for the projection (int8 hi/lo + s_hi, or bf16) into LDS.
+template <int WT, int BB>
+__device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, const int* sx, char* lds,
+                                                  const float (&racc)[BB], float cj) {
+  float* h = (float*)(lds + kOffH);
+  if (tid >= kThreads - kR) {
+    const int j = tid - (kThreads - kR);
+#pragma unroll
+    for (int b = 0; b < BB; ++b)
+      if (b < a.B) {
+        const float pre = (racc[b] + a.E[(size_t)sx[b] * kR + j]) + cj;
+        h[b * kR + j] = tanh_p(pre);
+      }
+  }
+  __syncthreads();
+  const int w = tid >> 6, lane = tid & 63;
+  for (int b = w; b < a.B; b += kWaves) {
+    const float4 u4 = *(const float4*)(h + b * kR + lane * 4);
+    if (WT == 0) {
+      const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+      uint32_t hi, lo;
+      const float s = quant4(u, &hi, &lo);
+      *(uint32_t*)(lds + kOffLat + (b * 2 + 0) * 256 + lane * 4) = hi;
+      *(uint32_t*)(lds + kOffLat + (b * 2 + 1) * 256 + lane * 4) = lo;
+      if (lane == 0) ((float*)(lds + kOffShi))[b] = s;
+    } else {
+      uint16_t* lb = (uint16_t*)(lds + kOffLat) + b * kR + lane * 4;
+      lb[0] = (uint16_t)bf16_rne(u4.x);
+      lb[1] = (uint16_t)bf16_rne(u4.y);
+      lb[2] = (uint16_t)bf16_rne(u4.z);
+      lb[3] = (uint16_t)bf16_rne(u4.w);
+    }
+  }
+  __syncthreads();
+}
+
+// Recurrent head: racc[b] = sum_k A[j][k] h[b][k], k ascending, one binary32
+// product and one binary32 add per term; A^T (bf16) and h live in LDS.
+template <int BB>
+__device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, const char* lds, float (&racc)[BB]) {
+  if (tid < kThreads - kR) return;
+  const int j = tid - (kThreads - kR);
+  const uint16_t* At = (const uint16_t*)(lds + kOffAt);
+  const float* h = (const float*)(lds + kOffH);
+#pragma unroll
+  for (int b = 0; b < BB; ++b) racc[b] = 0.0f;
+  for (int k = 0; k < kR; k += 4) {
+    float av[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) av[u] = bf16_f32(At[(k + u) * kR + j]);
+#pragma unroll
+    for (int b = 0; b < BB; ++b)
+      if (b < a.B) {
+        const float4 hv = *(const float4*)(h + b * kR + k);
+        float s = racc[b];
+        s = s + av[0] * hv.x;
+        s = s + av[1] * hv.y;
+        s = s + av[2] * hv.z;
+        s = s + av[3] * hv.w;
+        racc[b] = s;
+      }
+  }
+}
+
+// The whole walk in one cooperative launch: grid = one workgroup per CU.
+template <int WT, int BB, int HEAD, int TEMP>
+__global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
+  using Gm = Geo<WT, BB>;
+  using AT = typename AccT<WT>::T;
+  constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  unsigned long long* red = (unsigned long long*)(lds + kOffRed);
+  int* sx = (int*)(lds + kOffX);
+  int* sflag = (int*)(lds + kOffFlag);
+
+  const int tid = threadIdx.x, w = tid >> 6;
+  const Roles<WT, BB> ro(tid & 63);
+  const int g = blockIdx.x, G = gridDim.x;
+  const int tb = (int)((long long)g * a.tiles / G);
+  const int te = (int)((long long)(g + 1) * a.tiles / G);
+  const int cnt = te - tb;
+  const int nw = cnt > w ? (cnt - w + kWaves - 1) / kWaves : 0;
+  const int nreg = min(nw, a.reg_tiles);
+  const int nlds = min(nw - nreg, a.lds_tiles);
+  Ctrl* ctrl = a.ctrl;
+  const int par = a.parity;
+  const int scratch = HEAD == kHeadMarkov ? kScratchMarkov : kOffAt + kR * kR * 2;
+  char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
+
+  // The next walk on this context starts from cleared slots and counter.
+  if (g == 0) {
+    unsigned long long* ns = &ctrl->slot[par ^ 1][0][0];
+    for (int i = tid; i < kMaxSteps * kMaxB; i += kThreads) ns[i] = 0ull;
+    if (tid == 0) ctrl->arrive[par ^ 1] = 0u;
+  }
+
+  // One-time shard load (Fig. 4 entry cost): register tiles, then LDS tiles.
+  v4i wr[Gm::RT][Gm::CH];
+#pragma unroll
+  for (int i = 0; i < Gm::RT; ++i) {
+    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + kWaves * i) * Gm::CH * 64 + ro.lane;
+#pragma unroll
+    for (int c = 0; c < Gm::CH; ++c) wr[i][c] = (i < nreg) ? p[c * 64] : v4i{0, 0, 0, 0};
+  }
+  for (int i = 0; i < nlds; ++i) {
+    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + kWaves * (nreg + i)) * Gm::CH * 64 + ro.lane;
+#pragma unroll
+    for (int c = 0; c < Gm::CH; ++c) *(v4i*)(ldsw + (size_t)i * TB + c * 1024 + ro.lane * 16) = p[c * 64];
+  }
+  int gv[Gm::NG];
+  float gsw[Gm::NG];
+  bool gok[Gm::NG];
+#pragma unroll
+  for (int gi = 0; gi < Gm::NG; ++gi) {
+    const int i = gi * Gm::S + ro.cslot;
+    const int tile = tb + w + kWaves * i;
+    gv[gi] = tile * kTileRows + ro.n;
+    gok[gi] = i < nreg && gv[gi] < a.V;
+    gsw[gi] = (WT == 0 && gok[gi]) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
+  }
+
+  if (tid == 0) *sflag = 0;
+  float racc[BB];
+  float cj = 0.0f;
+  __syncthreads();
+  if (tid < a.B) {
+    int x = a.x0[tid];
+    if (x < 0 || x >= a.V) {
+      latch_error(ctrl, 6u);
+      *sflag = 1;
+      x = 0;
+    }
+    sx[tid] = x;
+  }
+  if (HEAD == kHeadRecurrent) {
+    uint16_t* At = (uint16_t*)(lds + kOffAt);
+    for (int i = tid; i < kR * kR; i += kThreads) At[(i % kR) * kR + i / kR] = a.A[i];
+    float* h = (float*)(lds + kOffH);
+    for (int i = tid; i < a.B * kR; i += kThreads) h[i] = a.h0[i];
+    if (tid >= kThreads - kR) cj = a.c[tid - (kThreads - kR)];
+  }
+  __syncthreads();
+  if (*sflag) return;
+  if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
+
+  for (int t = 0; t < a.gamma; ++t) {
+    // state -> latent (Markov: embedding row of x_t; recurrent: h_{t+1})
+    if (HEAD == kHeadRecurrent) recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj);
+    v4i Aop[Gm::NM][Gm::S][Gm::CH];
+    load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
+    float shi[Gm::NM][Gm::NE];
+#pragma unroll
+    for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+      for (int e = 0; e < Gm::NE; ++e) {
+        const int b = ro.bent(m, e);
+        shi[m][e] = 0.0f;
+        if (WT == 0 && b < a.B)
+          shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
+      }
+    unsigned long long best[Gm::NM][Gm::NE];
+#pragma unroll
+    for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+      for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0ull;
+
+    // projection over the register-resident tiles, S tiles per accumulator
+#pragma unroll
+    for (int gi = 0; gi < Gm::NG; ++gi) {
+      if (gi * Gm::S < nreg) {
+        uint32_t bv[Gm::NM][Gm::NE];
+#pragma unroll
+        for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, gv[gi], gok[gi], bv[m]);
+#pragma unroll
+        for (int m = 0; m < Gm::NM; ++m) {
+          AT acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < Gm::S; ++s) {
+            const int i = gi * Gm::S + s;
+            if (i < Gm::RT && i < nreg) {
+#pragma unroll
+              for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc);
+            }
+          }
+          epilogue<WT, BB, TEMP>(a, ro, t, m, acc, gv[gi], gok[gi], gsw[gi], bv[m], shi, best);
+        }
+      }
+    }
+    // LDS-resident and streamed tiles
+    stream_tiles<WT, BB, TEMP, kWaves>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, Aop, shi, best);
+
+    // Fig. 8: local winner -> device-scope max key and arrival count -> wait
+    // for every workgroup -> common winner.
+    reduce_to_lds<WT, BB>(a, ro, w, best, red);
+    __syncthreads();
+    if (w == 0) {
+      const int lane = ro.lane;
+      if (lane < a.B) {
+        unsigned long long k = 0ull;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) k = umax64(k, red[ww * kMaxB + lane]);
+        __hip_atomic_fetch_max(&ctrl->slot[par][t][lane], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) {
+        __hip_atomic_fetch_add(&ctrl->arrive[par], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned target = (unsigned)(t + 1) * (unsigned)G;
+        const long long t0 = wall_clock64();
+        while ((int)(__hip_atomic_load(&ctrl->arrive[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                     target) < 0) {
+          __builtin_amdgcn_s_sleep(1);
+          if (wall_clock64() - t0 > a.timeout_ticks) {
+            latch_error(ctrl, 5u);
+            *sflag = 1;
+            break;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (lane < a.B) {
+        const unsigned long long k =
+            __hip_atomic_load(&ctrl->slot[par][t][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int x = (int)(0xFFFFFFFFu - (uint32_t)k);
+        if (x < 0 || x >= a.V) {  // only after a failed barrier; keep every access in bounds
+          latch_error(ctrl, 5u);
+          *sflag = 1;
+          x = 0;
+        }
+        sx[lane] = x;
+        if (g == 0) a.tokens[lane * a.gamma + t] = x;
+      }
+    }
+    // recurrent: A h_{t+1} for the next step while wave 0 waits
+    if (HEAD == kHeadRecurrent && t + 1 < a.gamma) recurrent_matvec<BB>(a, tid, lds, racc);
+    __syncthreads();
+    if (*sflag) return;
+  }
+  if (HEAD == kHeadRecurrent && g == 0 && a.state) {
+    const float* h = (const float*)(lds + kOffH);
+    for (int i = tid; i < a.B * kR; i += kThreads) a.state[i] = h[i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// step-wise baseline: one launch per step, W streamed every step
+// ----------------------------------------------------------------------------
+
+constexpr int kStepWaves = 4;
+
+template <int WT, int BB, int TEMP>
+__global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
+  using Gm = Geo<WT, BB>;
+  __shared__ unsigned long long red[kWaves * kMaxB];
+  __shared__ int sx[kMaxB];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const Roles<WT, BB> ro(tid & 63);
+  const int g = blockIdx.x, G = gridDim.x;
+  const int t = a.step;
+  Ctrl* ctrl = a.ctrl;
+  const int par = a.parity;
+  if (t == 0 && g == 0) {
+    unsigned long long* ns = &ctrl->slot[par ^ 1][0][0];
+    for (int i = tid; i < kMaxSteps * kMaxB; i += blockDim.x) ns[i] = 0ull;
+    if (tid == 0) ctrl->arrive[par ^ 1] = 0u;
+  }
+  if (tid < a.B) {
+    int x;
+    if (t == 0) {
+      x = a.x0[tid];
+    } else {
+      const unsigned long long k =
+          __hip_atomic_load(&ctrl->slot[par][t - 1][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      x = (int)(0xFFFFFFFFu - (uint32_t)k);
+      if (g == 0) a.tokens[tid * a.gamma + t - 1] = x;
+    }
+    if (x < 0 || x >= a.V) {
+      latch_error(ctrl, 6u);
+      x = 0;
+    }
+    sx[tid] = x;
+  }
+  __syncthreads();
+  const int tb = (int)((long long)g * a.tiles / G);
+  const int te = (int)((long long)(g + 1) * a.tiles / G);
+  const int cnt = te - tb;
+  const int nw = cnt > w ? (cnt - w + kStepWaves - 1) / kStepWaves : 0;
+  v4i Aop[Gm::NM][Gm::S][Gm::CH];
+  load_latent<WT, BB, kHeadMarkov>(a, ro, sx, nullptr, Aop);
+  float shi[Gm::NM][Gm::NE];
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+    for (int e = 0; e < Gm::NE; ++e) {
+      const int b = ro.bent(m, e);
+      shi[m][e] = (WT == 0 && b < a.B) ? a.Es[sx[b]] : 0.0f;
+    }
+  unsigned long long best[Gm::NM][Gm::NE];
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+    for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0ull;
+  stream_tiles<WT, BB, TEMP, kStepWaves>(a, ro, t, tb, w, 0, 0, nw, nullptr, Aop, shi, best);
+  reduce_to_lds<WT, BB>(a, ro, w, best, red);
+  __syncthreads();
+  if (tid < a.B) {
+    unsigned long long k = 0ull;
+    for (int ww = 0; ww < kStepWaves; ++ww) k = umax64(k, red[ww * kMaxB + tid]);
+    __hip_atomic_fetch_max(&ctrl->slot[par][t][tid], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Last token of a step-wise walk.
+__global__ void finish_kernel(WalkArgs a) {
+  const int b = threadIdx.x;
+  if (b < a.B) {
+    const unsigned long long k =
+        __hip_atomic_load(&a.ctrl->slot[a.parity][a.gamma - 1][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.tokens[b * a.gamma + a.gamma - 1] = (int)(0xFFFFFFFFu - (uint32_t)k);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+
+hipError_t launch_repack_i8(const int8_t* W, const float* w_scale, int V, int tiles, int4* Wp,
+                            float* sw, hipStream_t s) {
+  const long long total = (long long)tiles * kChunksI8 * 64;
+  repack_i8_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(W, w_scale, V, tiles, Wp, sw);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_bf16(const uint16_t* W, int V, int tiles, int4* Wp, hipStream_t s) {
+  const long long total = (long long)tiles * kChunksBF * 64;
+  repack_bf16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(W, V, tiles, Wp);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const float* E, int V, int8_t* Eq, float* Es, hipStream_t s) {
+  quant_rows_kernel<<<(V + 3) / 4, 256, 0, s>>>(E, V, Eq, Es);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s) {
+  const long long n = (long long)V * kR;
+  bf16_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(E, n, Eb);
+  return hipGetLastError();
+}
+
+template <int WT, int BB, int HEAD, int TEMP>
+static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+  void* args[] = {(void*)&a};
+  return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads),
+                                    args, (unsigned)lds_bytes, s);
+}
+
+template <int WT, int HEAD, int TEMP>
+static hipError_t launch_walk_bb(int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+  switch (BB) {
+    case 1: return launch_walk_t<WT, 1, HEAD, TEMP>(a, grid, lds_bytes, s);
+    case 2: return launch_walk_t<WT, 2, HEAD, TEMP>(a, grid, lds_bytes, s);
+    case 4: return launch_walk_t<WT, 4, HEAD, TEMP>(a, grid, lds_bytes, s);
+    case 8: return launch_walk_t<WT, 8, HEAD, TEMP>(a, grid, lds_bytes, s);
+    case 16: return launch_walk_t<WT, 16, HEAD, TEMP>(a, grid, lds_bytes, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int WT, int HEAD>
+static hipError_t launch_walk_temp(int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+  return a.temperature ? launch_walk_bb<WT, HEAD, 1>(BB, a, grid, lds_bytes, s)
+                       : launch_walk_bb<WT, HEAD, 0>(BB, a, grid, lds_bytes, s);
+}
+
+hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+  if (wtype == 0)
+    return a.head == kHeadMarkov ? launch_walk_temp<0, kHeadMarkov>(BB, a, grid, lds_bytes, s)
+                                 : launch_walk_temp<0, kHeadRecurrent>(BB, a, grid, lds_bytes, s);
+  return a.head == kHeadMarkov ? launch_walk_temp<1, kHeadMarkov>(BB, a, grid, lds_bytes, s)
+                               : launch_walk_temp<1, kHeadRecurrent>(BB, a, grid, lds_bytes, s);
+}
+
+template <int WT, int TEMP>
+static hipError_t launch_step_t(int BB, const WalkArgs& a, int grid, hipStream_t s) {
+  const dim3 blk(kStepWaves * 64);
+  switch (BB) {
+    case 1: step_kernel<WT, 1, TEMP><<<grid, blk, 0, s>>>(a); break;
+    case 2: step_kernel<WT, 2, TEMP><<<grid, blk, 0, s>>>(a); break;
+    case 4: step_kernel<WT, 4, TEMP><<<grid, blk, 0, s>>>(a); break;
+    case 8: step_kernel<WT, 8, TEMP><<<grid, blk, 0, s>>>(a); break;
+    case 16: step_kernel<WT, 16, TEMP><<<grid, blk, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s) {
+  if (wtype == 0) return a.temperature ? launch_step_t<0, 1>(BB, a, grid, s) : launch_step_t<0, 0>(BB, a, grid, s);
+  return a.temperature ? launch_step_t<1, 1>(BB, a, grid, s) : launch_step_t<1, 0>(BB, a, grid, s);
+}
+
+hipError_t launch_finish(const WalkArgs& a, hipStream_t s) {
+  finish_kernel<<<1, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int WT, int HEAD, int TEMP>
+static hipError_t set_lds_attr(int lds_bytes) {
+  hipError_t e = hipSuccess;
+  const void* fns[] = {(const void*)walk_kernel<WT, 1, HEAD, TEMP>, (const void*)walk_kernel<WT, 2, HEAD, TEMP>,
+                       (const void*)walk_kernel<WT, 4, HEAD, TEMP>, (const void*)walk_kernel<WT, 8, HEAD, TEMP>,
+                       (const void*)walk_kernel<WT, 16, HEAD, TEMP>};
+  for (const void* f : fns) {
+    const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (r != hipSuccess) e = r;
+  }
+  return e;
+}
+
+hipError_t prepare_kernels(int lds_bytes) {
+  const hipError_t r[] = {
+      set_lds_attr<0, kHeadMarkov, 0>(lds_bytes), set_lds_attr<0, kHeadMarkov, 1>(lds_bytes),
+      set_lds_attr<0, kHeadRecurrent, 0>(lds_bytes), set_lds_attr<0, kHeadRecurrent, 1>(lds_bytes),
+      set_lds_attr<1, kHeadMarkov, 0>(lds_bytes), set_lds_attr<1, kHeadMarkov, 1>(lds_bytes),
+      set_lds_attr<1, kHeadRecurrent, 0>(lds_bytes), set_lds_attr<1, kHeadRecurrent, 1>(lds_bytes)};
+  for (hipError_t e : r)
+    if (e != hipSuccess) return e;
+  return hipSuccess;
+}
+
+}  // namespace wts

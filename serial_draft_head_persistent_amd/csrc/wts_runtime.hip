@@ -1,0 +1,302 @@
+// Host runtime of the walk-resident serial draft head: argument checks,
+// residency planning, create-time repacking, walk launches, error latch.
+//
+// "Weights That Stay" (arXiv 2611.00506) keeps each compute unit's shard of
+// the vocabulary projection on chip for the whole walk, fully or partially
+// (abstract, Fig. 1, Fig. 10, Fig. 14).  Here a 16-row tile is the unit of
+// residency: each wave keeps its first tiles in VGPRs, the next in LDS, and
+// streams the rest from memory at every step.
+
+#include <algorithm>
+#include <new>
+
+#include "wts.h"
+#include "wts_internal.h"
+
+using namespace wts;
+
+struct wts_ctx {
+  int device = 0;
+  int V = 0, head = 0, wtype = 0, tiles = 0, grid = 0;
+  int max_batch = 0, max_steps = 0;
+  int reg_cap = -1, lds_cap = -1;
+  int4* Wp = nullptr;
+  float* sw = nullptr;
+  int8_t* Eq = nullptr;
+  float* Es = nullptr;
+  uint16_t* Eb = nullptr;
+  const float* E = nullptr;
+  const uint16_t* A = nullptr;
+  const float* c = nullptr;
+  Ctrl* ctrl = nullptr;
+  unsigned long long walks = 0;
+  long long timeout_ticks = 0;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+int batch_bucket(int B) {
+  int bb = 1;
+  while (bb < B) bb <<= 1;
+  return bb;
+}
+
+int tile_bytes(int wtype) { return wtype == WTS_W_INT8 ? kTileBytesI8 : kTileBytesBF; }
+
+int lds_scratch(int head) { return head == WTS_HEAD_MARKOV ? 2048 : 32768 + kR * kR * 2; }
+
+// Residency plan for one batch bucket.
+void make_plan(const wts_ctx* ctx, int BB, int exec, wts_plan* p, int* lds_bytes) {
+  const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
+  const int per_wave = (per_wg + kWaves - 1) / kWaves;
+  int reg = std::min(reg_tiles_max(ctx->wtype, BB), per_wave);
+  if (ctx->reg_cap >= 0) reg = std::min(reg, ctx->reg_cap);
+  const int tb = tile_bytes(ctx->wtype);
+  const int scratch = lds_scratch(ctx->head);
+  int lds = std::max(0, (kLdsMax - scratch) / (kWaves * tb));
+  lds = std::min(lds, per_wave - reg);
+  if (ctx->lds_cap >= 0) lds = std::min(lds, ctx->lds_cap);
+  if (exec != WTS_EXEC_RESIDENT) reg = lds = 0;
+  p->grid = ctx->grid;
+  p->waves = kWaves;
+  p->tiles = ctx->tiles;
+  p->tiles_per_wave = per_wave;
+  p->reg_tiles = reg;
+  p->lds_tiles = lds;
+  p->stream_tiles = per_wave - reg - lds;
+  // exact on-chip bytes: count each wave's tiles
+  long long res_tiles = 0;
+  for (int g = 0; g < ctx->grid; ++g) {
+    const int cnt = (int)((long long)(g + 1) * ctx->tiles / ctx->grid) - (int)((long long)g * ctx->tiles / ctx->grid);
+    for (int w = 0; w < kWaves; ++w) {
+      const int nw = cnt > w ? (cnt - w + kWaves - 1) / kWaves : 0;
+      res_tiles += std::min(nw, reg + lds);
+    }
+  }
+  const long long esz = ctx->wtype == WTS_W_INT8 ? 1 : 2;
+  p->w_bytes = (long long)ctx->V * kR * esz;
+  p->resident_bytes = res_tiles * tb;
+  p->streamed_bytes = (long long)ctx->tiles * tb - p->resident_bytes;
+  *lds_bytes = std::min(kLdsMax, std::max(scratch + kWaves * lds * tb, 96 * 1024));
+}
+
+template <class T>
+wts_status dmalloc(T** p, size_t bytes) {
+  *p = nullptr;
+  if (hipMalloc((void**)p, bytes) != hipSuccess) {
+    *p = nullptr;
+    return WTS_ERR_NO_MEMORY;
+  }
+  return WTS_OK;
+}
+
+void free_ctx(wts_ctx* ctx) {
+  (void)hipFree(ctx->Wp);
+  (void)hipFree(ctx->sw);
+  (void)hipFree(ctx->Eq);
+  (void)hipFree(ctx->Es);
+  (void)hipFree(ctx->Eb);
+  (void)hipFree(ctx->ctrl);
+  delete ctx;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wts_status_string(wts_status s) {
+  switch (s) {
+    case WTS_OK: return "ok";
+    case WTS_ERR_INVALID_ARG: return "invalid argument";
+    case WTS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case WTS_ERR_NO_MEMORY: return "device allocation failed";
+    case WTS_ERR_DEVICE: return "HIP runtime or launch error";
+    case WTS_ERR_TIMEOUT: return "grid barrier watchdog expired";
+    case WTS_ERR_TOKEN_RANGE: return "initial token outside [0, V)";
+  }
+  return "unknown status";
+}
+
+wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
+  if (!p || !out) return WTS_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (p->V < 1 || p->V > 262143 || p->r < 1) return WTS_ERR_INVALID_ARG;
+  if (p->r != kR) return WTS_ERR_UNSUPPORTED;
+  if (p->head != WTS_HEAD_MARKOV && p->head != WTS_HEAD_RECURRENT) return WTS_ERR_INVALID_ARG;
+  if (p->wtype != WTS_W_INT8 && p->wtype != WTS_W_BF16) return WTS_ERR_INVALID_ARG;
+  if (!p->W || !p->E) return WTS_ERR_INVALID_ARG;
+  if (p->wtype == WTS_W_INT8 && !p->w_scale) return WTS_ERR_INVALID_ARG;
+  if (p->head == WTS_HEAD_RECURRENT && (!p->A || !p->c)) return WTS_ERR_INVALID_ARG;
+  if (p->max_batch < 1 || p->max_batch > kMaxB) return WTS_ERR_INVALID_ARG;
+  if (p->max_steps < 1 || p->max_steps > kMaxSteps) return WTS_ERR_INVALID_ARG;
+  if (p->resident_tiles < -1 || p->lds_tiles < -1) return WTS_ERR_INVALID_ARG;
+  if (((uintptr_t)p->W & 15) || ((uintptr_t)p->E & 15)) return WTS_ERR_INVALID_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev) return WTS_ERR_INVALID_ARG;
+  DeviceGuard guard(p->device);
+
+  int cus = 0, coop = 0, clock_khz = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, p->device) != hipSuccess ||
+      hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, p->device) != hipSuccess)
+    return WTS_ERR_DEVICE;
+  if (!coop || cus < 1) return WTS_ERR_UNSUPPORTED;
+
+  wts_ctx* ctx = new (std::nothrow) wts_ctx();
+  if (!ctx) return WTS_ERR_NO_MEMORY;
+  ctx->device = p->device;
+  ctx->V = p->V;
+  ctx->head = p->head;
+  ctx->wtype = p->wtype;
+  ctx->tiles = (p->V + kTileRows - 1) / kTileRows;
+  ctx->grid = cus;
+  ctx->max_batch = p->max_batch;
+  ctx->max_steps = p->max_steps;
+  ctx->reg_cap = p->resident_tiles;
+  ctx->lds_cap = p->lds_tiles;
+  ctx->E = p->E;
+  ctx->A = p->A;
+  ctx->c = p->c;
+  ctx->timeout_ticks = (long long)clock_khz * 1000LL * 2;  // 2 s per barrier wait
+
+  const size_t tb = tile_bytes(p->wtype);
+  wts_status st = dmalloc(&ctx->Wp, (size_t)ctx->tiles * tb);
+  if (st == WTS_OK) st = dmalloc(&ctx->ctrl, sizeof(Ctrl));
+  if (st == WTS_OK && p->wtype == WTS_W_INT8) st = dmalloc(&ctx->sw, (size_t)ctx->tiles * kTileRows * 4);
+  if (st == WTS_OK && p->head == WTS_HEAD_MARKOV && p->wtype == WTS_W_INT8) {
+    st = dmalloc(&ctx->Eq, (size_t)p->V * 512);
+    if (st == WTS_OK) st = dmalloc(&ctx->Es, (size_t)p->V * 4);
+  }
+  if (st == WTS_OK && p->head == WTS_HEAD_MARKOV && p->wtype == WTS_W_BF16)
+    st = dmalloc(&ctx->Eb, (size_t)p->V * kR * 2);
+  if (st != WTS_OK) {
+    free_ctx(ctx);
+    return st;
+  }
+  hipError_t e = hipMemset(ctx->ctrl, 0, sizeof(Ctrl));
+  if (e == hipSuccess) e = prepare_kernels(kLdsMax);
+  if (e == hipSuccess) {
+    if (p->wtype == WTS_W_INT8)
+      e = launch_repack_i8((const int8_t*)p->W, p->w_scale, p->V, ctx->tiles, ctx->Wp, ctx->sw, 0);
+    else
+      e = launch_repack_bf16((const uint16_t*)p->W, p->V, ctx->tiles, ctx->Wp, 0);
+  }
+  if (e == hipSuccess && ctx->Eq) e = launch_quant_rows(p->E, p->V, ctx->Eq, ctx->Es, 0);
+  if (e == hipSuccess && ctx->Eb) e = launch_bf16_rows(p->E, p->V, ctx->Eb, 0);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_ctx(ctx);
+    return WTS_ERR_DEVICE;
+  }
+  *out = ctx;
+  return WTS_OK;
+}
+
+wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, wts_plan* out) {
+  if (!ctx || !out || B < 1 || B > ctx->max_batch) return WTS_ERR_INVALID_ARG;
+  if (exec < WTS_EXEC_RESIDENT || exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
+  int lds_bytes = 0;
+  make_plan(ctx, batch_bucket(B), exec, out, &lds_bytes);
+  return WTS_OK;
+}
+
+wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
+  if (!ctx || !p) return WTS_ERR_INVALID_ARG;
+  if (p->B < 1 || p->B > ctx->max_batch || p->gamma < 1 || p->gamma > ctx->max_steps) return WTS_ERR_INVALID_ARG;
+  if (p->temperature != 0 && p->temperature != 1) return WTS_ERR_INVALID_ARG;
+  if (p->step_offset < 0 || p->reserved != 0) return WTS_ERR_INVALID_ARG;
+  if (p->exec < WTS_EXEC_RESIDENT || p->exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
+  if (!p->base || !p->x0 || !p->tokens_out) return WTS_ERR_INVALID_ARG;
+  if (ctx->head == WTS_HEAD_RECURRENT && !p->h0) return WTS_ERR_INVALID_ARG;
+  if (((uintptr_t)p->base & 1) || ((uintptr_t)p->x0 & 3) || ((uintptr_t)p->tokens_out & 3) ||
+      ((uintptr_t)p->logits_out & 1) || ((uintptr_t)p->h0 & 3) || ((uintptr_t)p->state_out & 3))
+    return WTS_ERR_INVALID_ARG;
+  if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
+  DeviceGuard guard(ctx->device);
+  const int BB = batch_bucket(p->B);
+  wts_plan plan;
+  int lds_bytes = 0;
+  make_plan(ctx, BB, p->exec, &plan, &lds_bytes);
+
+  WalkArgs a{};
+  a.Wp = ctx->Wp;
+  a.sw = ctx->sw;
+  a.Eq = ctx->Eq;
+  a.Es = ctx->Es;
+  a.Eb = ctx->Eb;
+  a.E = ctx->E;
+  a.A = ctx->A;
+  a.c = ctx->c;
+  a.ctrl = ctx->ctrl;
+  a.V = ctx->V;
+  a.tiles = ctx->tiles;
+  a.head = ctx->head;
+  a.reg_tiles = plan.reg_tiles;
+  a.lds_tiles = plan.lds_tiles;
+  a.B = p->B;
+  a.gamma = p->gamma;
+  a.step_offset = p->step_offset;
+  a.temperature = p->temperature;
+  a.seed_lo = (unsigned)(p->seed & 0xFFFFFFFFull);
+  a.seed_hi = (unsigned)(p->seed >> 32);
+  a.parity = (int)(ctx->walks & 1ull);
+  a.base = p->base;
+  a.x0 = p->x0;
+  a.h0 = p->h0;
+  a.tokens = p->tokens_out;
+  a.logits = p->logits_out;
+  a.state = p->state_out;
+  a.timeout_ticks = ctx->timeout_ticks;
+  hipStream_t s = (hipStream_t)p->stream;
+
+  hipError_t e;
+  if (p->exec == WTS_EXEC_STEPWISE) {
+    const int grid = std::max(1, (ctx->tiles + 7) / 8);
+    e = hipSuccess;
+    for (int t = 0; t < p->gamma && e == hipSuccess; ++t) {
+      a.step = t;
+      e = launch_step(ctx->wtype, BB, a, grid, s);
+    }
+    if (e == hipSuccess) e = launch_finish(a, s);
+  } else {
+    e = launch_walk(ctx->wtype, BB, a, ctx->grid, lds_bytes, s);
+  }
+  if (e != hipSuccess) return WTS_ERR_DEVICE;
+  ctx->walks++;
+  return WTS_OK;
+}
+
+wts_status wts_get_error(wts_ctx* ctx, int clear) {
+  if (!ctx) return WTS_ERR_INVALID_ARG;
+  DeviceGuard guard(ctx->device);
+  if (hipDeviceSynchronize() != hipSuccess) return WTS_ERR_DEVICE;
+  unsigned err = 0;
+  if (hipMemcpy(&err, &ctx->ctrl->err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return WTS_ERR_DEVICE;
+  if (clear && err) {
+    // A failed walk can leave its slots and counters in any state: start over.
+    if (hipMemset(ctx->ctrl, 0, sizeof(Ctrl)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      return WTS_ERR_DEVICE;
+    ctx->walks = 0;
+  }
+  return (wts_status)err;
+}
+
+void wts_destroy(wts_ctx* ctx) {
+  if (!ctx) return;
+  DeviceGuard guard(ctx->device);
+  (void)hipDeviceSynchronize();
+  free_ctx(ctx);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+"""Host-side helpers of the GPU tests: move seeded inputs to the device, run
+walks through the C ABI, and compare with the oracle."""
+import numpy as np
+
+
+def dev_inputs(d):
+    import torch
+    dev = torch.device("cuda", 0)
+    out = {}
+    if d["wtype"] == "int8":
+        out["W"] = torch.from_numpy(np.ascontiguousarray(d["W"])).to(dev)
+        out["w_scale"] = torch.from_numpy(d["s_w"]).to(dev)
+    else:
+        out["W"] = torch.from_numpy(d["W"].view(np.int16)).view(torch.bfloat16).to(dev)
+        out["w_scale"] = None
+    out["E"] = torch.from_numpy(d["E"]).to(dev)
+    out["base"] = torch.from_numpy(d["base"].view(np.int16)).view(torch.bfloat16).to(dev)
+    out["x0"] = torch.from_numpy(d["x0"].astype(np.int32)).to(dev)
+    if d["head"] == "recurrent":
+        out["A"] = torch.from_numpy(d["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+        out["c"] = torch.from_numpy(d["c"]).to(dev)
+        out["h0"] = torch.from_numpy(d["h0"]).to(dev)
+    else:
+        out["A"] = out["c"] = out["h0"] = None
+    return out
+
+
+def make_head(d, t=None, **kw):
+    from serial_draft_head_persistent_amd import Head
+    t = t or dev_inputs(d)
+    return Head(t["W"], t["E"], w_scale=t["w_scale"], A=t["A"], c=t["c"], head=d["head"], **kw), t
+
+
+def run(head, t, *, base=None, x0=None, h0=None, temperature=0, seed=0, step_offset=0, exec="resident",
+        logits=True, state=None):
+    import torch
+    base = t["base"] if base is None else base
+    x0 = t["x0"] if x0 is None else x0
+    h0 = t["h0"] if h0 is None else h0
+    state = (head.head == "recurrent") if state is None else state
+    o = head.walk(base, x0, h0=h0, temperature=temperature, seed=seed, step_offset=step_offset,
+                  logits=logits, state=state, exec=exec)
+    torch.cuda.synchronize()
+    err = head.error()
+    assert err == "WTS_OK", err
+    res = {"tokens": o["tokens"].cpu().numpy()}
+    if logits:
+        res["logits"] = o["logits"].view(torch.int16).cpu().numpy().view(np.uint16)
+    if state:
+        res["state"] = o["state"].cpu().numpy()
+    return res
+
+
+def oracle_walk(d, temperature=0, seed=0, step_offset=0, keep_z=False, base=None, x0=None, h0=None):
+    import oracle
+    return oracle.walk(d["W"], d["E"], d["base"] if base is None else base,
+                       d["x0"] if x0 is None else x0, wtype=d["wtype"], s_w=d["s_w"], head=d["head"],
+                       A=d["A"], c=d["c"], h0=d["h0"] if h0 is None else h0,
+                       temperature=temperature, seed=seed, step_offset=step_offset, keep_z=keep_z)
+
+
+def assert_exact(got, ref, what=""):
+    """int8 path: tokens and bf16 logit bits identical."""
+    tok_bad = np.argwhere(got["tokens"] != ref["tokens"])
+    assert tok_bad.size == 0, f"{what}: token mismatch at {tok_bad[:5].tolist()}: " \
+        f"gpu {got['tokens'][tuple(tok_bad[0])]} oracle {ref['tokens'][tuple(tok_bad[0])]}"
+    if "logits" in got and ref.get("logits") is not None:
+        bad = np.argwhere(got["logits"] != ref["logits"])
+        assert bad.size == 0, f"{what}: {len(bad)} logit mismatches, first at {bad[:3].tolist()}"
+    if "state" in got and ref.get("state") is not None:
+        assert np.array_equal(got["state"], ref["state"]), f"{what}: final state differs"
