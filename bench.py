@@ -1,0 +1,239 @@
+"""Benchmark of the serial draft walk on one MI355X.
+
+Workload (the headline configuration): Markov head, int8 W with per-row
+scales, V = 151,936, r = 256, B = 1, gamma = 16, greedy; W fully resident in
+one persistent kernel.  One "step" of this benchmark is one complete walk
+(gamma serial head steps) over one batch of synthetic input already resident
+in HBM.
+
+Prints one JSON line: microseconds per walk (lower is better), the per-step
+cost and entry cost fitted over gamma in {1, 7, 16}, achieved W-read
+bandwidth, the roofline of the dominant kernel, the CPU oracle on the host
+cores, and side measurements (batch and temperature sweep, bf16 248k,
+recurrent head, fused-streaming and step-wise execution).
+
+    python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0          # dense int8 MFMA, published (TOP/s)
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only: no sweeps, no CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only the timed headline walks (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def timed_walks(head, t, n, warmup, **kw):
+    """Total-event time of n back-to-back walks (ms per walk) and per-walk samples (us)."""
+    import torch
+    out = None
+    for _ in range(warmup):
+        out = head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        out = head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+    e1.record(s)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    # per-walk distribution
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(s)
+        out = head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+        b.record(s)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    err = head.error()
+    if err != "WTS_OK":
+        raise RuntimeError(err)
+    return total_ms / n, us
+
+
+def walk_stats(us):
+    return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+            "p90_us": float(np.percentile(us, 90))}
+
+
+def fit_steps(head, d, t, gammas=(1, 7, 16), n=100, warmup=10, **kw):
+    """Least-squares line over complete walks of gamma steps: slope = per-step cost, intercept = entry."""
+    import torch
+    med = []
+    for g in gammas:
+        tg = dict(t)
+        tg["base"] = t["base"][:, :g].contiguous()
+        _, us = timed_walks(head, tg, n, warmup, **kw)
+        med.append(float(np.median(us)))
+    A = np.vstack([np.array(gammas, float), np.ones(len(gammas))]).T
+    slope, icpt = np.linalg.lstsq(A, np.array(med), rcond=None)[0]
+    return {"gammas": list(gammas), "median_us": med, "per_step_us": float(slope), "entry_us": float(icpt)}
+
+
+def cpu_baseline(d, budget_s=12.0):
+    """The oracle (as it stands) on the host cores, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    walks, t0 = 0, time.perf_counter()
+    while True:
+        oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], keep_logits=False)
+        walks += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or walks >= 50:
+            break
+    return {"value": el / walks * 1e6, "unit": "us/walk", "cores": int(threads), "kind": "oracle",
+            "sample": f"{walks} complete walks of the headline workload (V=151936, B=1, gamma=16, greedy), "
+                      f"{el:.1f} s; int8 dot products via fp64 BLAS, epilogue single-threaded numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
+                          "(the walk's vocabulary sharding over several GPUs is a design note, not built)"}))
+        sys.exit(2)
+    import torch
+    import datagen
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import dev_inputs, make_head
+
+    dev_name = torch.cuda.get_device_name(0)
+    log("device", dev_name)
+    t_gen = time.perf_counter()
+    d = datagen.config_inputs(1)
+    t = dev_inputs(d)
+    log(f"inputs ready in {time.perf_counter() - t_gen:.1f} s")
+    head, t = make_head(d, t)
+    plan = head.plan(1)
+    log("plan", plan)
+
+    K, W = args.steps, args.warmup
+    ms_per_walk, us = timed_walks(head, t, K, W)
+    log(f"resident walk: {ms_per_walk * 1e3:.2f} us (mean over {K}), median {np.median(us):.2f} us")
+    if args.profile:
+        print(json.dumps({"metric": "us_per_walk", "value": ms_per_walk * 1e3}))
+        return
+
+    fit = fit_steps(head, d, t)
+    log("fit", fit)
+    V, r = d["V"], d["r"]
+    w_bytes = V * r
+    # algorithmic HBM bytes of one resident walk: one-time shard load of W and
+    # its row scales, base logits, the gamma gathered latent rows (512 B +
+    # scale), tokens out
+    gamma, B = d["gamma"], d["B"]
+    hbm_bytes = w_bytes + 4 * V + 2 * B * gamma * V + B * gamma * (512 + 4) + 4 * B * gamma
+    achieved = hbm_bytes / (ms_per_walk * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    per_step = {
+        "per_step_us": round(fit["per_step_us"], 3), "entry_us": round(fit["entry_us"], 3),
+        "w_read_GBps_per_step": round(w_bytes / (fit["per_step_us"] * 1e-6) / 1e9, 1),
+        "entry_w_load_GBps": round(w_bytes / (max(fit["entry_us"], 1e-3) * 1e-6) / 1e9, 1),
+    }
+
+    extras = {"walk": walk_stats(us), "fit_resident": fit, "plan": plan}
+    if not args.quick:
+        for ex in ("stream", "stepwise"):
+            extras[f"fit_{ex}"] = fit_steps(head, d, t, exec=ex)
+            log(ex, extras[f"fit_{ex}"])
+        # batch / temperature sweep on the same W (partial residency above B=4 is not needed here:
+        # the shard stays fully on chip, registers then LDS)
+        sweep = []
+        for B_ in (1, 2, 4, 8, 16):
+            dB = datagen.config_inputs(1, B=B_, gamma=16, seed=1)
+            import torch as _t
+            base = _t.from_numpy(dB["base"].view(np.int16)).view(_t.bfloat16).cuda()
+            x0 = _t.from_numpy(dB["x0"]).cuda()
+            for T in (0, 1):
+                tb = {"base": base, "x0": x0}
+                m, u = timed_walks(head, tb, 50, 5, temperature=T, seed=0)
+                sweep.append({"B": B_, "gamma": 16, "T": T, "median_us": round(float(np.median(u)), 2),
+                              "plan_reg_lds_stream": [head.plan(B_)[k] for k in ("reg_tiles", "lds_tiles", "stream_tiles")]})
+            log("sweep B", B_, sweep[-2:])
+        extras["sweep_markov_int8_v151936"] = sweep
+        head.close()
+        del t
+        torch.cuda.empty_cache()
+        # bf16 W, V = 248,320 (partial residency)
+        d3 = datagen.config_inputs(3, B=16, gamma=16)
+        h3, t3 = make_head(d3)
+        r3 = []
+        for B_ in (1, 4, 16):
+            tb = {"base": t3["base"][:B_].contiguous(), "x0": t3["x0"][:B_].contiguous()}
+            m, u = timed_walks(h3, tb, 50, 5)
+            p3 = h3.plan(B_)
+            r3.append({"B": B_, "median_us": round(float(np.median(u)), 2),
+                       "resident_MB": round(p3["resident_bytes"] / 1e6, 1),
+                       "streamed_MB_per_step": round(p3["streamed_bytes"] / 1e6, 1)})
+        extras["markov_bf16_v248320"] = r3
+        log("bf16 248k", r3)
+        h3.close()
+        del t3, d3
+        torch.cuda.empty_cache()
+        # recurrent head, 15 steps
+        d4 = datagen.config_inputs(4)
+        h4, t4 = make_head(d4)
+        m, u = timed_walks(h4, t4, 100, 10)
+        extras["recurrent_int8_v151936_g15"] = walk_stats(u)
+        log("recurrent", extras["recurrent_int8_v151936_g15"])
+        h4.close()
+        del t4, d4
+
+    cpu = None
+    if not (args.quick or args.no_cpu):
+        cpu = cpu_baseline(d)
+        log("cpu", cpu)
+
+    line = {
+        "metric": "us per gamma=16 draft walk (V=151936, r=256, B=1, int8 W resident, greedy)",
+        "value": round(ms_per_walk * 1e3, 3),
+        "unit": "us/walk",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_walk, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded Student-t(4) int8 W, N(0,1/256) E, N(0,2) bf16 base)",
+        "config": {"workload": "markov-int8-v151936-r256-b1-g16-greedy", "V": V, "r": r, "B": 1,
+                   "gamma": 16, "temperature": 0, "residency": "full",
+                   "device": dev_name},
+        "per_step": per_step,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

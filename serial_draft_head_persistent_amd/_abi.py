@@ -26,7 +26,7 @@ class CreateParams(ctypes.Structure):
     _fields_ = [("V", c_int32), ("r", c_int32), ("head", c_int32), ("wtype", c_int32),
                 ("W", c_void_p), ("w_scale", c_void_p), ("E", c_void_p), ("A", c_void_p), ("c", c_void_p),
                 ("max_batch", c_int32), ("max_steps", c_int32), ("resident_tiles", c_int32),
-                ("lds_tiles", c_int32), ("device", c_int32)]
+                ("lds_tiles", c_int32), ("device", c_int32), ("cooperative", c_int32)]
 
 
 class WalkParams(ctypes.Structure):
@@ -55,6 +55,12 @@ class WtsError(RuntimeError):
 def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run python -m serial_draft_head_persistent_amd.build")
+    # torch ships its own HIP runtime, referenced by a different file name but
+    # with the same soname as the system one libwts.so links.  Loading torch
+    # first makes libwts.so bind to that already-loaded runtime, so the
+    # process has one HIP runtime and torch's device pointers and streams are
+    # valid in the library.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.wts_create.argtypes = [P(CreateParams), P(c_void_p)]

@@ -32,14 +32,22 @@ constexpr int kLdsMax = 163840;
 constexpr int kHeadMarkov = 0;
 constexpr int kHeadRecurrent = 1;
 
-// Device control block of one context.  Zeroed at create; afterwards each
-// walk (parity k & 1) clears the slots and counter of the next walk (parity
-// (k + 1) & 1) before it touches its own, so no host-side reset is needed.
+constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most
+constexpr int kGroups = 16;     // first level of the cross-workgroup selection
+constexpr int kSub = 16;        // step-wise path: sub-slots per (step, batch row)
+
+// Device control block of one context.  Every array has a leading walk
+// parity: walk k uses parity k & 1, and the first launch of walk k clears
+// the arrays of parity (k + 1) & 1 for the next walk, so no host-side reset
+// is needed between walks.
 struct Ctrl {
-  unsigned long long slot[2][kMaxSteps][kMaxB];  // per walk parity: max keys
-  unsigned int arrive[2];                        // per walk parity: arrivals
-  unsigned int err;                              // latched wts_status
-  unsigned int pad[61];
+  // persistent walk, two-level all-gather of tagged keys (step parity second)
+  unsigned long long l1[2][2][kMaxGrid][kMaxB];   // one line per workgroup
+  unsigned long long l2[2][2][kGroups][kMaxB];    // one line per group
+  // step-wise walk: device-scope max per (step, batch row, sub-slot)
+  unsigned long long ss[2][kMaxSteps][kMaxB][kSub];
+  unsigned int err;                               // latched wts_status
+  unsigned int pad[63];
 };
 
 struct WalkArgs {
@@ -83,7 +91,7 @@ hipError_t launch_repack_bf16(const uint16_t* W, int V, int tiles, int4* Wp, hip
 hipError_t launch_quant_rows(const float* E, int V, int8_t* Eq, float* Es, hipStream_t s);
 hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s);
 hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes,
-                       hipStream_t s);
+                       bool cooperative, hipStream_t s);
 hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s);
 hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);

@@ -21,9 +21,12 @@
 //    64 lanes of the result carry useful logits;
 //  * W tiles live in VGPRs (registers), then LDS, and the remainder streams
 //    from HBM each step with one tile of prefetch;
-//  * the grid barrier is a device-scope atomic max on a per-step slot, an
-//    arrival counter with release order, and one spinning lane per
-//    workgroup with s_sleep back-off and a wall-clock watchdog.
+//  * the cross-workgroup selection is a two-level all-gather of step-tagged
+//    64-bit keys through device memory (one line per workgroup, a group
+//    leader per 16 workgroups, one line per group), polled by one wave per
+//    workgroup with a wall-clock watchdog.  On MI355X a single-address atomic
+//    maximum plus an arrival counter serialises 2 x 256 device-scope atomics
+//    per step (measured ~11 us per step); the all-gather needs none.
 //
 // Bit-exactness with the host reference needs: no contraction of a*b+c
 // (built with -ffp-contract=off), IEEE division (default), rintf half-even.
@@ -49,15 +52,19 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 }
 __device__ __forceinline__ float bf16_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Selection key (Fig. 8, "packs its local winner"): the high word orders
-// binary32 scores (-0 folded into +0), the low word is 0xFFFFFFFF - v so the
-// lowest index wins among equal scores.  0 is below every key.
+// Selection key (Fig. 8, "packs its local winner"): bits 49..18 order the
+// binary32 scores (-0 folded into +0), bits 17..0 hold 0x3FFFF - v so the
+// lowest index wins among equal scores (V < 2^18).  0 is below every key.
+// Bits 63..57 are left free for the step tag of the cross-workgroup exchange.
+constexpr unsigned long long kKeyMask = (1ull << 50) - 1;
+constexpr int kTagShift = 57;
 __device__ __forceinline__ unsigned long long sel_key(float s, int v) {
   uint32_t b = __float_as_uint(s);
   if (b == 0x80000000u) b = 0u;
   const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+  return ((unsigned long long)o << 18) | (unsigned long long)(0x3FFFFu - (uint32_t)v);
 }
+__device__ __forceinline__ int key_token(unsigned long long k) { return (int)(0x3FFFFu - (uint32_t)(k & 0x3FFFFu)); }
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
@@ -494,6 +501,96 @@ __device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
   atomicCAS(&ctrl->err, 0u, code);
 }
 
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Clear the control arrays of the next walk (parity par ^ 1), spread over
+// the whole grid.  Nothing in this walk touches them.
+__device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
+  const int q = par ^ 1;
+  const size_t n1 = sizeof(ctrl->l1[0]) / 8, n2 = sizeof(ctrl->l2[0]) / 8, n3 = sizeof(ctrl->ss[0]) / 8;
+  unsigned long long* p1 = &ctrl->l1[q][0][0][0];
+  unsigned long long* p2 = &ctrl->l2[q][0][0][0];
+  unsigned long long* p3 = &ctrl->ss[q][0][0][0];
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2 + n3; i += stride) {
+    if (i < n1) p1[i] = 0ull;
+    else if (i < n1 + n2) p2[i - n1] = 0ull;
+    else p3[i - n1 - n2] = 0ull;
+  }
+}
+
+// Cross-workgroup selection of one step (Fig. 8), one wave per workgroup.
+// Every workgroup publishes its local winner key per batch row, tagged with
+// the step, in its own line; the first workgroup of each of kGroups groups
+// waits for its members' keys and publishes the group maximum; every
+// workgroup waits for the kGroups group maxima and takes the overall
+// maximum.  The keys carry the token, so no other data has to be made
+// visible: relaxed device-scope loads and stores suffice.  Returns false if
+// the watchdog expired.  On return, lanes b < B hold the winning key of row b.
+template <int BB>
+__device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsigned long long key,
+                                         long long timeout, unsigned long long* winner) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x, G = gridDim.x;
+  const unsigned long long want = (unsigned long long)(t + 1);
+  const unsigned long long tag = want << kTagShift;
+  unsigned long long* L1 = &ctrl->l1[par][t & 1][0][0];
+  unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0];
+  if (lane < B) st_agent(&L1[g * kMaxB + lane], tag | key);
+  const int grp = g % kGroups;
+  const long long t0 = wall_clock64();
+  bool ok_all = true;
+  if (g < kGroups) {
+    const int nmem = (G - grp + kGroups - 1) / kGroups;
+    unsigned long long best;
+    while (true) {
+      bool ok = true;
+      best = 0ull;
+      for (int q = lane; q < nmem * BB; q += 64) {
+        const int i = q / BB, b = q % BB;
+        if (b < B) {
+          const unsigned long long v = ld_agent(&L1[(grp + kGroups * i) * kMaxB + b]);
+          ok = ok && (v >> kTagShift) == want;
+          best = umax64(best, v);
+        }
+      }
+      if (__all(ok)) break;
+      if (wall_clock64() - t0 > timeout) {
+        ok_all = false;
+        break;
+      }
+    }
+#pragma unroll
+    for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
+    if (ok_all && lane < B) st_agent(&L2[grp * kMaxB + lane], best);
+  }
+  const int ngr = G < kGroups ? G : kGroups;
+  unsigned long long best = 0ull;
+  while (ok_all) {
+    bool ok = true;
+    best = 0ull;
+    for (int q = lane; q < ngr * BB; q += 64) {
+      const int x = q / BB, b = q % BB;
+      if (b < B) {
+        const unsigned long long v = ld_agent(&L2[x * kMaxB + b]);
+        ok = ok && (v >> kTagShift) == want;
+        best = umax64(best, v);
+      }
+    }
+    if (__all(ok)) break;
+    if (wall_clock64() - t0 > timeout) ok_all = false;
+  }
+#pragma unroll
+  for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
+  *winner = best & kKeyMask;
+  return ok_all;
+}
+
 // Recurrent head, first half of a step (Fig. 13): h_{t+1} = tanh(A h_t +
 // E[x_t] + c) with the A h_t sums (ascending k) already in acc; then the
 // latent rows for the projection (int8 hi/lo + s_hi, or bf16) into LDS.
@@ -585,12 +682,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   const int scratch = HEAD == kHeadMarkov ? kScratchMarkov : kOffAt + kR * kR * 2;
   char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
 
-  // The next walk on this context starts from cleared slots and counter.
-  if (g == 0) {
-    unsigned long long* ns = &ctrl->slot[par ^ 1][0][0];
-    for (int i = tid; i < kMaxSteps * kMaxB; i += kThreads) ns[i] = 0ull;
-    if (tid == 0) ctrl->arrive[par ^ 1] = 0u;
-  }
+  clear_next_walk(ctrl, par);
 
   // One-time shard load (Fig. 4 entry cost): register tiles, then LDS tiles.
   v4i wr[Gm::RT][Gm::CH];
@@ -693,33 +785,21 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     __syncthreads();
     if (w == 0) {
       const int lane = ro.lane;
+      unsigned long long k = 0ull;
       if (lane < a.B) {
-        unsigned long long k = 0ull;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) k = umax64(k, red[ww * kMaxB + lane]);
-        __hip_atomic_fetch_max(&ctrl->slot[par][t][lane], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (lane == 0) {
-        __hip_atomic_fetch_add(&ctrl->arrive[par], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned target = (unsigned)(t + 1) * (unsigned)G;
-        const long long t0 = wall_clock64();
-        while ((int)(__hip_atomic_load(&ctrl->arrive[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                     target) < 0) {
-          __builtin_amdgcn_s_sleep(1);
-          if (wall_clock64() - t0 > a.timeout_ticks) {
-            latch_error(ctrl, 5u);
-            *sflag = 1;
-            break;
-          }
-        }
+      unsigned long long win;
+      const bool ok = exchange<BB>(ctrl, par, t, a.B, k, a.timeout_ticks, &win);
+      if (!ok && lane == 0) {
+        latch_error(ctrl, 5u);
+        *sflag = 1;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (lane < a.B) {
-        const unsigned long long k =
-            __hip_atomic_load(&ctrl->slot[par][t][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int x = (int)(0xFFFFFFFFu - (uint32_t)k);
-        if (x < 0 || x >= a.V) {  // only after a failed barrier; keep every access in bounds
-          latch_error(ctrl, 5u);
+        int x = key_token(win);
+        if (!ok || x < 0 || x >= a.V) {  // only after a failed exchange; keep every access in bounds
+          if (ok) latch_error(ctrl, 5u);
           *sflag = 1;
           x = 0;
         }
@@ -755,19 +835,16 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   const int t = a.step;
   Ctrl* ctrl = a.ctrl;
   const int par = a.parity;
-  if (t == 0 && g == 0) {
-    unsigned long long* ns = &ctrl->slot[par ^ 1][0][0];
-    for (int i = tid; i < kMaxSteps * kMaxB; i += blockDim.x) ns[i] = 0ull;
-    if (tid == 0) ctrl->arrive[par ^ 1] = 0u;
-  }
+  if (t == 0) clear_next_walk(ctrl, par);
   if (tid < a.B) {
     int x;
     if (t == 0) {
       x = a.x0[tid];
     } else {
-      const unsigned long long k =
-          __hip_atomic_load(&ctrl->slot[par][t - 1][tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      x = (int)(0xFFFFFFFFu - (uint32_t)k);
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int i = 0; i < kSub; ++i) k = umax64(k, ld_agent(&ctrl->ss[par][t - 1][tid][i]));
+      x = key_token(k);
       if (g == 0) a.tokens[tid * a.gamma + t - 1] = x;
     }
     if (x < 0 || x >= a.V) {
@@ -802,7 +879,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   if (tid < a.B) {
     unsigned long long k = 0ull;
     for (int ww = 0; ww < kStepWaves; ++ww) k = umax64(k, red[ww * kMaxB + tid]);
-    __hip_atomic_fetch_max(&ctrl->slot[par][t][tid], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(&ctrl->ss[par][t][tid][g % kSub], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -810,9 +887,10 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
 __global__ void finish_kernel(WalkArgs a) {
   const int b = threadIdx.x;
   if (b < a.B) {
-    const unsigned long long k =
-        __hip_atomic_load(&a.ctrl->slot[a.parity][a.gamma - 1][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.tokens[b * a.gamma + a.gamma - 1] = (int)(0xFFFFFFFFu - (uint32_t)k);
+    unsigned long long k = 0ull;
+    for (int i = 0; i < kSub; ++i) k = umax64(k, ld_agent(&a.ctrl->ss[a.parity][a.gamma - 1][b][i]));
+    const int x = key_token(k);
+    a.tokens[b * a.gamma + a.gamma - 1] = (x >= 0 && x < a.V) ? x : 0;
   }
 }
 
@@ -844,37 +922,46 @@ hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s) 
   return hipGetLastError();
 }
 
+// The persistent kernel needs all `grid` workgroups resident at once.  With
+// grid <= CUs and more than half of a CU's LDS per workgroup, a plain launch
+// places one workgroup per CU on an otherwise idle GPU; the cooperative
+// launch guarantees it but costs ~18 us more per launch on MI355X.  Either
+// way a workgroup that waits too long in the exchange latches WTS_ERR_TIMEOUT
+// and exits, so the grid always drains.
 template <int WT, int BB, int HEAD, int TEMP>
-static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads),
-                                    args, (unsigned)lds_bytes, s);
+  if (coop)
+    return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads),
+                                      args, (unsigned)lds_bytes, s);
+  return hipLaunchKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads), args,
+                         (size_t)lds_bytes, s);
 }
 
 template <int WT, int HEAD, int TEMP>
-static hipError_t launch_walk_bb(int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+static hipError_t launch_walk_bb(int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   switch (BB) {
-    case 1: return launch_walk_t<WT, 1, HEAD, TEMP>(a, grid, lds_bytes, s);
-    case 2: return launch_walk_t<WT, 2, HEAD, TEMP>(a, grid, lds_bytes, s);
-    case 4: return launch_walk_t<WT, 4, HEAD, TEMP>(a, grid, lds_bytes, s);
-    case 8: return launch_walk_t<WT, 8, HEAD, TEMP>(a, grid, lds_bytes, s);
-    case 16: return launch_walk_t<WT, 16, HEAD, TEMP>(a, grid, lds_bytes, s);
+    case 1: return launch_walk_t<WT, 1, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
+    case 2: return launch_walk_t<WT, 2, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
+    case 4: return launch_walk_t<WT, 4, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
+    case 8: return launch_walk_t<WT, 8, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
+    case 16: return launch_walk_t<WT, 16, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int WT, int HEAD>
-static hipError_t launch_walk_temp(int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
-  return a.temperature ? launch_walk_bb<WT, HEAD, 1>(BB, a, grid, lds_bytes, s)
-                       : launch_walk_bb<WT, HEAD, 0>(BB, a, grid, lds_bytes, s);
+static hipError_t launch_walk_temp(int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
+  return a.temperature ? launch_walk_bb<WT, HEAD, 1>(BB, a, grid, lds_bytes, coop, s)
+                       : launch_walk_bb<WT, HEAD, 0>(BB, a, grid, lds_bytes, coop, s);
 }
 
-hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes, hipStream_t s) {
+hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   if (wtype == 0)
-    return a.head == kHeadMarkov ? launch_walk_temp<0, kHeadMarkov>(BB, a, grid, lds_bytes, s)
-                                 : launch_walk_temp<0, kHeadRecurrent>(BB, a, grid, lds_bytes, s);
-  return a.head == kHeadMarkov ? launch_walk_temp<1, kHeadMarkov>(BB, a, grid, lds_bytes, s)
-                               : launch_walk_temp<1, kHeadRecurrent>(BB, a, grid, lds_bytes, s);
+    return a.head == kHeadMarkov ? launch_walk_temp<0, kHeadMarkov>(BB, a, grid, lds_bytes, coop, s)
+                                 : launch_walk_temp<0, kHeadRecurrent>(BB, a, grid, lds_bytes, coop, s);
+  return a.head == kHeadMarkov ? launch_walk_temp<1, kHeadMarkov>(BB, a, grid, lds_bytes, coop, s)
+                               : launch_walk_temp<1, kHeadRecurrent>(BB, a, grid, lds_bytes, coop, s);
 }
 
 template <int WT, int TEMP>

@@ -20,6 +20,7 @@ struct wts_ctx {
   int V = 0, head = 0, wtype = 0, tiles = 0, grid = 0;
   int max_batch = 0, max_steps = 0;
   int reg_cap = -1, lds_cap = -1;
+  bool cooperative = false;
   int4* Wp = nullptr;
   float* sw = nullptr;
   int8_t* Eq = nullptr;
@@ -151,7 +152,8 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
       hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, p->device) != hipSuccess ||
       hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, p->device) != hipSuccess)
     return WTS_ERR_DEVICE;
-  if (!coop || cus < 1) return WTS_ERR_UNSUPPORTED;
+  if (cus < 1 || (p->cooperative && !coop)) return WTS_ERR_UNSUPPORTED;
+  if (p->cooperative != 0 && p->cooperative != 1) return WTS_ERR_INVALID_ARG;
 
   wts_ctx* ctx = new (std::nothrow) wts_ctx();
   if (!ctx) return WTS_ERR_NO_MEMORY;
@@ -160,7 +162,8 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   ctx->head = p->head;
   ctx->wtype = p->wtype;
   ctx->tiles = (p->V + kTileRows - 1) / kTileRows;
-  ctx->grid = cus;
+  ctx->grid = std::min(cus, kMaxGrid);
+  ctx->cooperative = p->cooperative != 0;
   ctx->max_batch = p->max_batch;
   ctx->max_steps = p->max_steps;
   ctx->reg_cap = p->resident_tiles;
@@ -270,7 +273,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
     }
     if (e == hipSuccess) e = launch_finish(a, s);
   } else {
-    e = launch_walk(ctx->wtype, BB, a, ctx->grid, lds_bytes, s);
+    e = launch_walk(ctx->wtype, BB, a, ctx->grid, lds_bytes, ctx->cooperative, s);
   }
   if (e != hipSuccess) return WTS_ERR_DEVICE;
   ctx->walks++;
