@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the timed headline walks (for rocprofv3 runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
+                         "of a --profile --copy-calib run into profiles/" + "walk_traffic.json and exit")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="with --profile: also run a plain 512 MiB device copy (known bytes) so a counter "
+                         "run can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -94,6 +100,78 @@ def fit_steps(head, d, t, gammas=(1, 7, 16), n=100, warmup=10, **kw):
     return {"gammas": list(gammas), "median_us": med, "per_step_us": float(slope), "entry_us": float(icpt)}
 
 
+WALLCLOCK_MHZ = 100.0   # s_memrealtime rate on MI355X (hipDeviceAttributeWallClockRate)
+COPY_BYTES = 512 << 20  # the --copy-calib copy
+HEADLINE_KERNEL = "walk_kernel<0, 1, 0, 0>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("wts_kernels.hip", "wts_internal.h"):
+        with open(os.path.join(ROOT, "serial_draft_head_persistent_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Per-dispatch HBM bytes of the headline kernel from two counter runs, each
+    scaled by what the same counter reads for a plain copy of known size."""
+    import csv
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        walk = [float(r["Counter_Value"]) for r in rows if HEADLINE_KERNEL in r["Kernel_Name"]]
+        calib_kib = max(copies)            # the 512 MiB copies are the largest copy dispatches
+        factor = COPY_BYTES / (calib_kib * 1024.0)
+        out[name] = {"walk_kib_per_dispatch": sum(walk) / len(walk), "dispatches": len(walk),
+                     "copy_kib": calib_kib, "copy_bytes": COPY_BYTES, "scale": factor,
+                     "walk_bytes_per_dispatch": sum(walk) / len(walk) * 1024.0 * factor}
+    res = {"kernel": HEADLINE_KERNEL, "workload": "markov-int8-v151936-r256-b1-g16-greedy",
+           "source_sha256": kernel_source_hash(), "counters": out,
+           "traffic_bytes_per_launch": out["FETCH_SIZE"]["walk_bytes_per_dispatch"]
+           + out["WRITE_SIZE"]["walk_bytes_per_dispatch"]}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+def committed_traffic():
+    """Traffic of the headline kernel from the committed counter summary, or
+    None if the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def breakdown(head, t, reps=20, **kw):
+    """Per-step phase times from the kernel's wall-clock stamps (Fig. 13b analog)."""
+    import torch
+    out = None
+    rows = []
+    for _ in range(reps):
+        out = head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, trace=True, **kw)
+        torch.cuda.synchronize()
+        rows.append(out["trace"].cpu().numpy().astype(np.float64) / WALLCLOCK_MHZ)
+    tr = np.stack(rows)                       # [reps, gamma, grid, 4] in us
+    lat = tr[..., 1] - tr[..., 0]
+    proj = tr[..., 2] - tr[..., 1]
+    exch = tr[..., 3] - tr[..., 2]
+    step = tr[:, 1:, :, 0] - tr[:, :-1, :, 0]
+    skew = tr[..., 2].max(axis=2) - tr[..., 2].min(axis=2)   # spread of local-winner-ready times
+    med = lambda x: round(float(np.median(x)), 3)
+    return {"latent_us": med(lat), "project_epilogue_reduce_us": med(proj), "exchange_us": med(exch),
+            "step_us": med(step), "arrival_skew_us": med(skew),
+            "exchange_us_p90": round(float(np.percentile(exch, 90)), 3)}
+
+
 def cpu_baseline(d, budget_s=12.0):
     """The oracle (as it stands) on the host cores, on a bounded sample of the same workload."""
     import oracle
@@ -116,6 +194,9 @@ def cpu_baseline(d, budget_s=12.0):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
                           "(the walk's vocabulary sharding over several GPUs is a design note, not built)"}))
@@ -136,6 +217,14 @@ def main():
     log("plan", plan)
 
     K, W = args.steps, args.warmup
+    if args.copy_calib:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 536870912 bytes")
+        del src, dst
     ms_per_walk, us = timed_walks(head, t, K, W)
     log(f"resident walk: {ms_per_walk * 1e3:.2f} us (mean over {K}), median {np.median(us):.2f} us")
     if args.profile:
@@ -152,8 +241,12 @@ def main():
     gamma, B = d["gamma"], d["B"]
     hbm_bytes = w_bytes + 4 * V + 2 * B * gamma * V + B * gamma * (512 + 4) + 4 * B * gamma
     achieved = hbm_bytes / (ms_per_walk * 1e-3) / 1e9
+    traffic = committed_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic / (ms_per_walk * 1e-3) / 1e9, 1),
+                "algorithmic_bytes_per_launch": int(hbm_bytes),
+                "traffic_bytes_per_launch": None if traffic is None else int(traffic)}
     per_step = {
         "per_step_us": round(fit["per_step_us"], 3), "entry_us": round(fit["entry_us"], 3),
         "w_read_GBps_per_step": round(w_bytes / (fit["per_step_us"] * 1e-6) / 1e9, 1),
@@ -161,6 +254,10 @@ def main():
     }
 
     extras = {"walk": walk_stats(us), "fit_resident": fit, "plan": plan}
+    extras["breakdown_resident"] = breakdown(head, t)
+    log("breakdown resident", extras["breakdown_resident"])
+    extras["breakdown_stream"] = breakdown(head, t, exec="stream")
+    log("breakdown stream", extras["breakdown_stream"])
     if not args.quick:
         for ex in ("stream", "stepwise"):
             extras[f"fit_{ex}"] = fit_steps(head, d, t, exec=ex)

@@ -100,6 +100,11 @@ typedef struct wts_walk_params {
   int32_t exec;           /* WTS_EXEC_*                                        */
   int32_t reserved;       /* must be 0                                         */
   void* stream;           /* hipStream_t (NULL = default stream)               */
+  int64_t* trace_out;     /* device, [gamma][grid][4] int64, or NULL.  Persistent
+                             executions only: per step and workgroup, wall-clock
+                             stamps (100 MHz ticks) at step start, latent
+                             loaded, local winner ready, common winner known.
+                             Per-step breakdown in the manner of Fig. 13b.     */
 } wts_walk_params;
 
 typedef struct wts_plan {

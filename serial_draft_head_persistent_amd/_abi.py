@@ -33,7 +33,7 @@ class WalkParams(ctypes.Structure):
     _fields_ = [("B", c_int32), ("gamma", c_int32), ("step_offset", c_int32), ("temperature", c_int32),
                 ("seed", c_uint64), ("base", c_void_p), ("x0", c_void_p), ("h0", c_void_p),
                 ("tokens_out", c_void_p), ("logits_out", c_void_p), ("state_out", c_void_p),
-                ("exec", c_int32), ("reserved", c_int32), ("stream", c_void_p)]
+                ("exec", c_int32), ("reserved", c_int32), ("stream", c_void_p), ("trace_out", c_void_p)]
 
 
 class Plan(ctypes.Structure):

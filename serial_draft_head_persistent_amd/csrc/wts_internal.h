@@ -17,7 +17,7 @@ constexpr int kMaxSteps = 64;
 // batches need more registers for latents and keys, so they keep fewer tiles
 // in registers and more in LDS.
 constexpr int reg_tiles_max(int wtype, int BB) {
-  return wtype == 0 ? (BB >= 8 ? 3 : 5) : 2;
+  return wtype == 0 ? (BB <= 2 ? 5 : BB == 4 ? 4 : BB == 8 ? 3 : 2) : 1;
 }
 constexpr int kChunksI8 = 4;      // 16-byte lane chunks per int8 tile (64 k each)
 constexpr int kChunksBF = 8;      // 16-byte lane chunks per bf16 tile (32 k each)
@@ -34,6 +34,7 @@ constexpr int kHeadRecurrent = 1;
 
 constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most
 constexpr int kGroups = 16;     // first level of the cross-workgroup selection
+constexpr int kCopies = 8;      // copies of the second-level lines (one per XCD)
 constexpr int kSub = 16;        // step-wise path: sub-slots per (step, batch row)
 
 // Device control block of one context.  Every array has a leading walk
@@ -43,7 +44,7 @@ constexpr int kSub = 16;        // step-wise path: sub-slots per (step, batch ro
 struct Ctrl {
   // persistent walk, two-level all-gather of tagged keys (step parity second)
   unsigned long long l1[2][2][kMaxGrid][kMaxB];   // one line per workgroup
-  unsigned long long l2[2][2][kGroups][kMaxB];    // one line per group
+  unsigned long long l2[2][2][kCopies][kGroups][kMaxB];  // one line per group and copy
   // step-wise walk: device-scope max per (step, batch row, sub-slot)
   unsigned long long ss[2][kMaxSteps][kMaxB][kSub];
   unsigned int err;                               // latched wts_status
@@ -81,6 +82,7 @@ struct WalkArgs {
   int* tokens;
   uint16_t* logits;
   float* state;
+  long long* trace;        // [gamma][grid][4] phase stamps or null
   long long timeout_ticks; // watchdog, in s_memrealtime ticks (100 MHz)
 };
 

@@ -335,8 +335,75 @@ struct Roles {
   __device__ __forceinline__ int arow_hl(int m) const { return (m * Gm::RPS + aw) % Gm::LPB; }
 };
 
-// Latent of this step as MFMA A operands: slot s holds the latent rows in A
-// rows [s*RPS, (s+1)*RPS) and zeros elsewhere.
+// ---- workgroup-local selection keys ----
+// Inside a workgroup a key orders (score, -row) with the row counted from the
+// workgroup's first vocabulary row: T=0 uses 32 bits (16-bit order of the
+// bf16 logit, 16-bit row), T=1 64 bits (32-bit order of the fp32 score).
+// 0 means "no candidate".  -0 is folded into +0.
+template <int TEMP> struct LKey { typedef uint32_t T; };
+template <> struct LKey<1> { typedef unsigned long long T; };
+
+__device__ __forceinline__ uint32_t ord16(uint32_t h) {
+  h = (h == 0x8000u) ? 0u : h;
+  return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t ord32(uint32_t b) {
+  b = (b == 0x80000000u) ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t kmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// Workgroup-local key -> device-wide key (same layout as sel_key: order of
+// the fp32 score in bits 49..18, 0x3FFFF - v in bits 17..0).
+__device__ __forceinline__ unsigned long long global_key(uint32_t k, int row0) {
+  if (k == 0u) return 0ull;
+  const uint32_t o16 = k >> 16;
+  const uint32_t o32 = (o16 << 16) | ((o16 & 0x8000u) ? 0u : 0xFFFFu);  // order of the widened bf16
+  const uint32_t v = (uint32_t)row0 + (0xFFFFu - (k & 0xFFFFu));
+  return ((unsigned long long)o32 << 18) | (unsigned long long)(0x3FFFFu - v);
+}
+__device__ __forceinline__ unsigned long long global_key(unsigned long long k, int row0) {
+  if (k == 0ull) return 0ull;
+  const uint32_t o32 = (uint32_t)(k >> 16);
+  const uint32_t v = (uint32_t)row0 + (0xFFFFu - (uint32_t)(k & 0xFFFFu));
+  return ((unsigned long long)o32 << 18) | (unsigned long long)(0x3FFFFu - v);
+}
+
+// Max over the 16 lanes of each DPP row (butterfly of quad and mirror moves).
+#define WTS_DPP(x, c) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (c), 0xF, 0xF, false))
+__device__ __forceinline__ uint32_t row_max(uint32_t x) {
+  x = kmax(x, WTS_DPP(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = kmax(x, WTS_DPP(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = kmax(x, WTS_DPP(x, 0x141));  // row_half_mirror
+  x = kmax(x, WTS_DPP(x, 0x140));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ unsigned long long row_max(unsigned long long x) {
+#define WTS_DPP64(x, c) \
+  (((unsigned long long)WTS_DPP((uint32_t)((x) >> 32), (c)) << 32) | WTS_DPP((uint32_t)(x), (c)))
+  x = kmax(x, WTS_DPP64(x, 0xB1));
+  x = kmax(x, WTS_DPP64(x, 0x4E));
+  x = kmax(x, WTS_DPP64(x, 0x141));
+  x = kmax(x, WTS_DPP64(x, 0x140));
+#undef WTS_DPP64
+  return x;
+}
+__device__ __forceinline__ uint32_t readlane(uint32_t x, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+__device__ __forceinline__ unsigned long long readlane(unsigned long long x, int l) {
+  return ((unsigned long long)readlane((uint32_t)(x >> 32), l) << 32) | readlane((uint32_t)x, l);
+}
+
+// 1 KiB of zeros in device memory: the A-operand source of the lanes whose
+// row is not in the slot being loaded.
+__device__ __attribute__((aligned(64))) int4 g_zero_page[64];
+
+// Latent of this step as MFMA A operands.  Slot s holds the latent rows in A
+// rows [s*RPS, (s+1)*RPS) and zeros elsewhere: every lane loads each slot's
+// 16-byte chunks either from its latent row (its own slot) or from the zero
+// page (other slots), so building the operands costs loads, not VALU work.
 template <int WT, int BB, int HEAD>
 __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, BB>& ro, const int* sx,
                                             const char* lds, v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH]) {
@@ -346,23 +413,28 @@ __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, B
     const int b = ro.arow_b(m);
     const bool ok = b < a.B;
     const int hl = ro.arow_hl(m);
-    v4i d[Gm::CH];
     if (HEAD == kHeadMarkov) {
       const int x = ok ? sx[b] : 0;
       const v4i* src = WT == 0 ? (const v4i*)(a.Eq + (size_t)x * 512 + hl * 256 + ro.q * 16)
                                : (const v4i*)(a.Eb + (size_t)x * kR + ro.q * 8);
+      const v4i* zero = (const v4i*)g_zero_page;
 #pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) d[c] = ok ? src[c * 4] : v4i{0, 0, 0, 0};
+      for (int s = 0; s < Gm::S; ++s) {
+        const v4i* p = (ok && ro.aslot == s) ? src : zero;
+#pragma unroll
+        for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = p[c * 4];
+      }
     } else {
       const char* src = WT == 0 ? lds + kOffLat + (b * 2 + hl) * 256 + ro.q * 16
                                 : lds + kOffLat + (b * kR + ro.q * 8) * 2;
+      v4i d[Gm::CH];
 #pragma unroll
       for (int c = 0; c < Gm::CH; ++c) d[c] = ok ? *(const v4i*)(src + c * 64) : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < Gm::S; ++s)
+#pragma unroll
+        for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = (ro.aslot == s) ? d[c] : v4i{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int s = 0; s < Gm::S; ++s)
-#pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = (ro.aslot == s) ? d[c] : v4i{0, 0, 0, 0};
   }
 }
 
@@ -370,33 +442,39 @@ __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, B
 // selection (Fig. 8 step 1): logit = bf16(((acc_hi s_hi + acc_lo s_lo) s_w) +
 // base) for int8 W, bf16(acc + base) for bf16 W; score = logit (T=0) or
 // logit + Gumbel noise (T=1); keep the largest key per batch entry.
+// Branch-free: lanes without a valid (row, batch) pair contribute key 0.
 template <int WT, int BB, int TEMP>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
-                                         const typename AccT<WT>::T& acc, int v, bool ok, float sw,
-                                         const uint32_t (&bv)[Geo<WT, BB>::NE],
+                                         const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
+                                         float sw, const uint32_t (&bv)[Geo<WT, BB>::NE],
                                          const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
-                                         unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+                                         typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
     const int b = ro.bent(m, e);
-    if (ok && b < a.B) {
-      float z;
-      if (WT == 0) {
-        const float zh = (float)acc[2 * e] * shi[m][e];
-        const float zl = (float)acc[2 * e + 1] * (shi[m][e] * 0.00390625f);
-        z = zh + zl;
-        z = z * sw;
-      } else {
-        z = acc[e];
-      }
-      z = z + bf16_f32(bv[e]);
-      const uint32_t lg = bf16_rne(z);
-      if (a.logits) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
-      float sc = bf16_f32(lg);
-      if (TEMP) sc = sc + gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
-      best[m][e] = umax64(best[m][e], sel_key(sc, v));
+    if (b >= BB) continue;  // compile-time: entry unused by this batch bucket
+    const bool okb = ok && b < a.B;
+    float z;
+    if (WT == 0) {
+      const float zh = (float)acc[2 * e] * shi[m][e];
+      const float zl = (float)acc[2 * e + 1] * (shi[m][e] * 0.00390625f);
+      z = zh + zl;
+      z = z * sw;
+    } else {
+      z = acc[e];
     }
+    z = z + bf16_f32(bv[e]);
+    const uint32_t lg = bf16_rne(z);
+    if (a.logits && okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
+    typename LKey<TEMP>::T k;
+    if (TEMP == 0) {
+      k = (ord16(lg) << 16) | lrow;
+    } else {
+      const float sc = bf16_f32(lg) + gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
+      k = ((unsigned long long)ord32(__float_as_uint(sc)) << 16) | lrow;
+    }
+    best[m][e] = kmax(best[m][e], okb ? k : (typename LKey<TEMP>::T)0);
   }
 }
 
@@ -408,93 +486,100 @@ __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
     const int b = ro.bent(m, e);
-    bv[e] = (ok && b < a.B) ? (uint32_t)a.base[((size_t)b * a.gamma + t) * a.V + v] : 0u;
+    bv[e] = (b < BB && ok && b < a.B) ? (uint32_t)a.base[((size_t)b * a.gamma + t) * a.V + v] : 0u;
   }
 }
 
-// Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), read from LDS
-// for i < i0 + nlds and from memory otherwise, with one tile of prefetch.
+// One W tile that is not register-resident, with its row scale and base
+// logits, as loaded one tile ahead of its use.
+template <int WT, int BB>
+struct TileBuf {
+  v4i w[Geo<WT, BB>::CH];
+  float sw;
+  uint32_t bv[Geo<WT, BB>::NM][Geo<WT, BB>::NE];
+};
+
+// Load wave-local tile i (from LDS for i < i0 + nlds, else from memory) for
+// step t.  Lanes whose C-slot is 0 own the tile's vocabulary rows.
+template <int WT, int BB, int NWV>
+__device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb, int w,
+                                           int i, int i0, int nlds, const char* ldsw, TileBuf<WT, BB>& d) {
+  using Gm = Geo<WT, BB>;
+  constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
+  const int tile = tb + w + NWV * i;
+  if (i < i0 + nlds) {
+    const char* p = ldsw + (size_t)(i - i0) * TB + ro.lane * 16;
+#pragma unroll
+    for (int c = 0; c < Gm::CH; ++c) d.w[c] = *(const v4i*)(p + c * 1024);
+  } else {
+    const v4i* p = (const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane;
+#pragma unroll
+    for (int c = 0; c < Gm::CH; ++c) d.w[c] = p[c * 64];
+  }
+  const int v = tile * kTileRows + ro.n;
+  const bool ok = ro.cslot == 0 && v < a.V;
+  d.sw = (WT == 0 && ok) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, d.bv[m]);
+}
+
+// Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), one tile of
+// prefetch.  `cur` holds tile i0 of this step, loaded before the step began.
 template <int WT, int BB, int TEMP, int NWV>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
+                                             TileBuf<WT, BB> cur,
                                              const v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH],
                                              const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
-                                             unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+                                             typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
   using Gm = Geo<WT, BB>;
   using AT = typename AccT<WT>::T;
-  constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
-  if (i0 >= nw) return;
-  v4i cur[Gm::CH];
-  float csw = 0.0f;
-  uint32_t cbv[Gm::NM][Gm::NE];
-  auto fetch = [&](int i, v4i (&dst)[Gm::CH], float& dsw, uint32_t (&dbv)[Gm::NM][Gm::NE]) {
-    const int tile = tb + w + NWV * i;
-    if (i < i0 + nlds) {
-      const char* p = ldsw + (size_t)(i - i0) * TB + ro.lane * 16;
-#pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) dst[c] = *(const v4i*)(p + c * 1024);
-    } else {
-      const v4i* p = (const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane;
-#pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) dst[c] = p[c * 64];
-    }
-    const int v = tile * kTileRows + ro.n;
-    const bool ok = ro.cslot == 0 && v < a.V;
-    dsw = (WT == 0 && ok) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
-#pragma unroll
-    for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, dbv[m]);
-  };
-  fetch(i0, cur, csw, cbv);
   for (int i = i0; i < nw; ++i) {
-    v4i nxt[Gm::CH];
-    float nsw = 0.0f;
-    uint32_t nbv[Gm::NM][Gm::NE];
-    if (i + 1 < nw) fetch(i + 1, nxt, nsw, nbv);
+    TileBuf<WT, BB> nxt;
+    if (i + 1 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 1, i0, nlds, ldsw, nxt);
     const int tile = tb + w + NWV * i;
     const int v = tile * kTileRows + ro.n;
     const bool ok = ro.cslot == 0 && v < a.V;
+    const uint32_t lrow = 0xFFFFu - (uint32_t)((tile - tb) * kTileRows + ro.n);
 #pragma unroll
     for (int m = 0; m < Gm::NM; ++m) {
       AT acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][0][c], cur[c], acc);
-      epilogue<WT, BB, TEMP>(a, ro, t, m, acc, v, ok, csw, cbv[m], shi, best);
+      for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][0][c], cur.w[c], acc);
+      epilogue<WT, BB, TEMP>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best);
     }
-    if (i + 1 < nw) {
-#pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) cur[c] = nxt[c];
-      csw = nsw;
-#pragma unroll
-      for (int m = 0; m < Gm::NM; ++m)
-#pragma unroll
-        for (int e = 0; e < Gm::NE; ++e) cbv[m][e] = nbv[m][e];
-    }
+    if (i + 1 < nw) cur = nxt;
   }
 }
 
-// Wave reduction of the keys of lanes that hold the same batch rows, then
-// one representative lane per batch row writes red[w][b].
-template <int WT, int BB>
-__device__ __forceinline__ void reduce_to_lds(const WalkArgs& a, const Roles<WT, BB>& ro, int w,
-                                              unsigned long long (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+// Wave-level reduction of the keys (Fig. 8 step 2): DPP maximum inside each
+// 16-lane row, then the four rows' maxima per batch row via readlane; lane 0
+// writes red[w][b] for b < BB.
+template <int WT, int BB, int TEMP>
+__device__ __forceinline__ void reduce_to_lds(const Roles<WT, BB>& ro, int w,
+                                              typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                               unsigned long long* red) {
   using Gm = Geo<WT, BB>;
+  using K = typename LKey<TEMP>::T;
+  K acc_b[BB];
+#pragma unroll
+  for (int b = 0; b < BB; ++b) acc_b[b] = 0;
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
     for (int e = 0; e < Gm::NE; ++e) {
-      unsigned long long k = best[m][e];
+      const K k = row_max(best[m][e]);
 #pragma unroll
-      for (int s = 1; s < 16; s <<= 1) k = umax64(k, shfl_xor_u64(k, s));
-      if (Gm::RPS == 4) {
-        k = umax64(k, shfl_xor_u64(k, 16));
-        k = umax64(k, shfl_xor_u64(k, 32));
-      } else if (Gm::RPS == 8) {
-        k = umax64(k, shfl_xor_u64(k, 32));
+      for (int q = 0; q < 4; ++q) {
+        const int cw0 = (4 * q) % Gm::RPS;
+        const int b = WT == 0 ? (m * Gm::RPS + cw0) / 2 + e : m * Gm::RPS + cw0 + e;
+        if (b < BB) acc_b[b] = kmax(acc_b[b], readlane(k, 16 * q));
       }
-      const int b = ro.bent(m, e);
-      if (ro.n == 0 && ro.q < Gm::RPS / 4 && b < a.B) red[w * kMaxB + b] = k;
     }
+  if (ro.lane == 0) {
+#pragma unroll
+    for (int b = 0; b < BB; ++b) red[w * kMaxB + b] = (unsigned long long)acc_b[b];
+  }
 }
 
 __device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
@@ -514,7 +599,7 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
   const int q = par ^ 1;
   const size_t n1 = sizeof(ctrl->l1[0]) / 8, n2 = sizeof(ctrl->l2[0]) / 8, n3 = sizeof(ctrl->ss[0]) / 8;
   unsigned long long* p1 = &ctrl->l1[q][0][0][0];
-  unsigned long long* p2 = &ctrl->l2[q][0][0][0];
+  unsigned long long* p2 = &ctrl->l2[q][0][0][0][0];
   unsigned long long* p3 = &ctrl->ss[q][0][0][0];
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2 + n3; i += stride) {
@@ -527,9 +612,10 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
 // Cross-workgroup selection of one step (Fig. 8), one wave per workgroup.
 // Every workgroup publishes its local winner key per batch row, tagged with
 // the step, in its own line; the first workgroup of each of kGroups groups
-// waits for its members' keys and publishes the group maximum; every
-// workgroup waits for the kGroups group maxima and takes the overall
-// maximum.  The keys carry the token, so no other data has to be made
+// waits for its members' keys and publishes the group maximum in kCopies
+// copies; every workgroup waits for the kGroups group maxima in copy
+// (g % kCopies) -- the copy read by the workgroups of its XCD under the
+// round-robin dispatch -- and takes the overall maximum.  The keys carry the token, so no other data has to be made
 // visible: relaxed device-scope loads and stores suffice.  Returns false if
 // the watchdog expired.  On return, lanes b < B hold the winning key of row b.
 template <int BB>
@@ -540,7 +626,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
   const unsigned long long want = (unsigned long long)(t + 1);
   const unsigned long long tag = want << kTagShift;
   unsigned long long* L1 = &ctrl->l1[par][t & 1][0][0];
-  unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0];
+  unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0][0];
   if (lane < B) st_agent(&L1[g * kMaxB + lane], tag | key);
   const int grp = g % kGroups;
   const long long t0 = wall_clock64();
@@ -567,7 +653,13 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     }
 #pragma unroll
     for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
-    if (ok_all && lane < B) st_agent(&L2[grp * kMaxB + lane], best);
+    if (ok_all) {
+      // after the butterfly every lane holds the maximum of row (lane % BB)
+      for (int q = lane; q < kCopies * BB; q += 64) {
+        const int r = q / BB, b = q % BB;
+        if (b < B) st_agent(&L2[(r * kGroups + grp) * kMaxB + b], best);
+      }
+    }
   }
   const int ngr = G < kGroups ? G : kGroups;
   unsigned long long best = 0ull;
@@ -577,7 +669,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     for (int q = lane; q < ngr * BB; q += 64) {
       const int x = q / BB, b = q % BB;
       if (b < B) {
-        const unsigned long long v = ld_agent(&L2[x * kMaxB + b]);
+        const unsigned long long v = ld_agent(&L2[((g % kCopies) * kGroups + x) * kMaxB + b]);
         ok = ok && (v >> kTagShift) == want;
         best = umax64(best, v);
       }
@@ -657,6 +749,33 @@ __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, con
   }
 }
 
+// While wave 0 exchanges keys, wave 1 reads the embedding row of this
+// workgroup's local winner (one word per 128-byte line).  One of these rows
+// is the next step's latent; reading it now brings it into the device-side
+// cache, so the gather after the exchange does not wait for HBM.
+template <int WT, int HEAD, int TEMP>
+__device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned long long* red, int row0,
+                                              int lane, char* lds_dummy) {
+  constexpr int LINES = HEAD == kHeadMarkov ? (WT == 0 ? 5 : 4) : 8;  // 128-byte lines per row
+  uint32_t acc = 0;
+  for (int q = lane; q < a.B * LINES; q += 64) {
+    const int b = q / LINES, j = q % LINES;
+    typename LKey<TEMP>::T lk = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + b]);
+    const int v = key_token(global_key(lk, row0));
+    if (v >= 0 && v < a.V) {
+      if (HEAD == kHeadMarkov && WT == 0)
+        acc ^= j < 4 ? *(const uint32_t*)(a.Eq + (size_t)v * 512 + j * 128) : __float_as_uint(a.Es[v]);
+      else if (HEAD == kHeadMarkov)
+        acc ^= *(const uint32_t*)(a.Eb + (size_t)v * kR + j * 64);
+      else
+        acc ^= __float_as_uint(a.E[(size_t)v * kR + j * 32]);
+    }
+  }
+  if (acc == 0x9E3779B9u) *lds_dummy = 1;  // keeps the loads; the byte is never read
+}
+
 // The whole walk in one cooperative launch: grid = one workgroup per CU.
 template <int WT, int BB, int HEAD, int TEMP>
 __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
@@ -708,6 +827,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     gok[gi] = i < nreg && gv[gi] < a.V;
     gsw[gi] = (WT == 0 && gok[gi]) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
   }
+  const int row0 = tb * kTileRows;  // first vocabulary row of this workgroup
 
   if (tid == 0) *sflag = 0;
   float racc[BB];
@@ -733,11 +853,27 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
 
+  // Base logits of the register-resident groups and the first non-register
+  // tile are loaded one step ahead, so their memory latency overlaps the
+  // previous step's exchange.
+  uint32_t bnx[Gm::NG][Gm::NM][Gm::NE];
+  auto fetch_base = [&](int t) {
+#pragma unroll
+    for (int gi = 0; gi < Gm::NG; ++gi)
+#pragma unroll
+      for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, gv[gi], gok[gi], bnx[gi][m]);
+  };
+  fetch_base(0);
+
+  // per-step phase stamps (workgroup view of wave 0)
+  auto stamp = [&](int t, int k) {
+    if (a.trace && tid == 0) a.trace[((size_t)t * G + g) * 4 + k] = wall_clock64();
+  };
   for (int t = 0; t < a.gamma; ++t) {
+    stamp(t, 0);
     // state -> latent (Markov: embedding row of x_t; recurrent: h_{t+1})
     if (HEAD == kHeadRecurrent) recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj);
-    v4i Aop[Gm::NM][Gm::S][Gm::CH];
-    load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
+    // scales of the latent rows (int8), issued with the latent gather
     float shi[Gm::NM][Gm::NE];
 #pragma unroll
     for (int m = 0; m < Gm::NM; ++m)
@@ -745,22 +881,28 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
       for (int e = 0; e < Gm::NE; ++e) {
         const int b = ro.bent(m, e);
         shi[m][e] = 0.0f;
-        if (WT == 0 && b < a.B)
+        if (WT == 0 && b < BB && b < a.B)
           shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
       }
-    unsigned long long best[Gm::NM][Gm::NE];
+    // first non-register tile of this step: its load overlaps the register tiles' work
+    TileBuf<WT, BB> first;
+    if (nreg < nw) fetch_tile<WT, BB, kWaves>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
+    v4i Aop[Gm::NM][Gm::S][Gm::CH];
+    load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
+    if (a.trace) {
+      __builtin_amdgcn_s_waitcnt(0);
+      stamp(t, 1);
+    }
+    typename LKey<TEMP>::T best[Gm::NM][Gm::NE];
 #pragma unroll
     for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
-      for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0ull;
+      for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0;
 
     // projection over the register-resident tiles, S tiles per accumulator
 #pragma unroll
     for (int gi = 0; gi < Gm::NG; ++gi) {
       if (gi * Gm::S < nreg) {
-        uint32_t bv[Gm::NM][Gm::NE];
-#pragma unroll
-        for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, gv[gi], gok[gi], bv[m]);
 #pragma unroll
         for (int m = 0; m < Gm::NM; ++m) {
           AT acc = {0, 0, 0, 0};
@@ -772,23 +914,29 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
               for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc);
             }
           }
-          epilogue<WT, BB, TEMP>(a, ro, t, m, acc, gv[gi], gok[gi], gsw[gi], bv[m], shi, best);
+          epilogue<WT, BB, TEMP>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0), gok[gi],
+                                 gsw[gi], bnx[gi][m], shi, best);
         }
       }
     }
     // LDS-resident and streamed tiles
-    stream_tiles<WT, BB, TEMP, kWaves>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, Aop, shi, best);
+    if (nreg < nw) stream_tiles<WT, BB, TEMP, kWaves>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best);
+    if (t + 1 < a.gamma) fetch_base(t + 1);
 
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
     // for every workgroup -> common winner.
-    reduce_to_lds<WT, BB>(a, ro, w, best, red);
+    reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
     __syncthreads();
+    stamp(t, 2);
+    if (w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP>(a, red, row0, ro.lane, lds + kOffFlag + 4);
     if (w == 0) {
       const int lane = ro.lane;
       unsigned long long k = 0ull;
       if (lane < a.B) {
+        typename LKey<TEMP>::T lk = 0;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) k = umax64(k, red[ww * kMaxB + lane]);
+        for (int ww = 0; ww < kWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + lane]);
+        k = global_key(lk, row0);
       }
       unsigned long long win;
       const bool ok = exchange<BB>(ctrl, par, t, a.B, k, a.timeout_ticks, &win);
@@ -806,6 +954,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
         sx[lane] = x;
         if (g == 0) a.tokens[lane * a.gamma + t] = x;
       }
+      stamp(t, 3);
     }
     // recurrent: A h_{t+1} for the next step while wave 0 waits
     if (HEAD == kHeadRecurrent && t + 1 < a.gamma) recurrent_matvec<BB>(a, tid, lds, racc);
@@ -858,27 +1007,32 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   const int te = (int)((long long)(g + 1) * a.tiles / G);
   const int cnt = te - tb;
   const int nw = cnt > w ? (cnt - w + kStepWaves - 1) / kStepWaves : 0;
-  v4i Aop[Gm::NM][Gm::S][Gm::CH];
-  load_latent<WT, BB, kHeadMarkov>(a, ro, sx, nullptr, Aop);
   float shi[Gm::NM][Gm::NE];
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
     for (int e = 0; e < Gm::NE; ++e) {
       const int b = ro.bent(m, e);
-      shi[m][e] = (WT == 0 && b < a.B) ? a.Es[sx[b]] : 0.0f;
+      shi[m][e] = (WT == 0 && b < BB && b < a.B) ? a.Es[sx[b]] : 0.0f;
     }
-  unsigned long long best[Gm::NM][Gm::NE];
+  v4i Aop[Gm::NM][Gm::S][Gm::CH];
+  load_latent<WT, BB, kHeadMarkov>(a, ro, sx, nullptr, Aop);
+  typename LKey<TEMP>::T best[Gm::NM][Gm::NE];
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
-    for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0ull;
-  stream_tiles<WT, BB, TEMP, kStepWaves>(a, ro, t, tb, w, 0, 0, nw, nullptr, Aop, shi, best);
-  reduce_to_lds<WT, BB>(a, ro, w, best, red);
+    for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0;
+  if (nw > 0) {
+    TileBuf<WT, BB> first;
+    fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
+    stream_tiles<WT, BB, TEMP, kStepWaves>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best);
+  }
+  reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
   __syncthreads();
   if (tid < a.B) {
-    unsigned long long k = 0ull;
-    for (int ww = 0; ww < kStepWaves; ++ww) k = umax64(k, red[ww * kMaxB + tid]);
+    typename LKey<TEMP>::T lk = 0;
+    for (int ww = 0; ww < kStepWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + tid]);
+    const unsigned long long k = global_key(lk, tb * kTileRows);
     __hip_atomic_fetch_max(&ctrl->ss[par][t][tid][g % kSub], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

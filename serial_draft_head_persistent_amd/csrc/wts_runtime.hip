@@ -223,7 +223,8 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   if (!p->base || !p->x0 || !p->tokens_out) return WTS_ERR_INVALID_ARG;
   if (ctx->head == WTS_HEAD_RECURRENT && !p->h0) return WTS_ERR_INVALID_ARG;
   if (((uintptr_t)p->base & 1) || ((uintptr_t)p->x0 & 3) || ((uintptr_t)p->tokens_out & 3) ||
-      ((uintptr_t)p->logits_out & 1) || ((uintptr_t)p->h0 & 3) || ((uintptr_t)p->state_out & 3))
+      ((uintptr_t)p->logits_out & 1) || ((uintptr_t)p->h0 & 3) || ((uintptr_t)p->state_out & 3) ||
+      ((uintptr_t)p->trace_out & 7))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
   DeviceGuard guard(ctx->device);
@@ -260,6 +261,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.tokens = p->tokens_out;
   a.logits = p->logits_out;
   a.state = p->state_out;
+  a.trace = (long long*)p->trace_out;
   a.timeout_ticks = ctx->timeout_ticks;
   hipStream_t s = (hipStream_t)p->stream;
 
