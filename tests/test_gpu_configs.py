@@ -1,0 +1,163 @@
+"""GPU parity at the full workload sizes (V=151,936 int8, V=248,320 bf16),
+invariants of the walk, and edge cases, all through the C ABI."""
+import numpy as np
+import pytest
+
+import datagen
+from conftest import cached_inputs
+from gpu_helpers import make_head, run, oracle_walk, assert_exact, assert_bf16_close, dev_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(**kw):
+    print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.fixture(scope="module")
+def head152():
+    d = cached_inputs(2)                       # V=151,936, B=16, gamma=16
+    h, t = make_head(d)
+    yield d, h, t
+    h.close()
+
+
+def _slice(d, t, B, gamma):
+    ds = dict(d)
+    ds["base"] = d["base"][:B, :gamma]
+    ds["x0"] = d["x0"][:B]
+    ts = dict(t)
+    ts["base"] = t["base"][:B, :gamma].contiguous()
+    ts["x0"] = t["x0"][:B].contiguous()
+    return ds, ts
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("T", [0, 1])
+def test_config2_full_size_exact(head152, B, T):
+    d, h, t = head152
+    _case(cfg=2, B=B, gamma=16, T=T)
+    ds, ts = _slice(d, t, B, 16)
+    assert_exact(run(h, ts, temperature=T, seed=0), oracle_walk(ds, temperature=T, seed=0), f"B={B} T={T}")
+
+
+@pytest.mark.parametrize("B,gamma", [(1, 1), (1, 7), (16, 1), (16, 7), (3, 7)])
+def test_config2_short_walks_exact(head152, B, gamma):
+    d, h, t = head152
+    _case(cfg=2, B=B, gamma=gamma, T=1)
+    ds, ts = _slice(d, t, B, gamma)
+    assert_exact(run(h, ts, temperature=1, seed=11), oracle_walk(ds, temperature=1, seed=11), f"B={B} g={gamma}")
+
+
+def test_execution_modes_identical_full_size(head152):
+    d, h, t = head152
+    _case(cfg=2, B=4, modes="resident/stream/stepwise")
+    ds, ts = _slice(d, t, 4, 16)
+    ref = run(h, ts, temperature=1, seed=5)
+    for ex in ("stream", "stepwise"):
+        got = run(h, ts, temperature=1, seed=5, exec=ex)
+        assert np.array_equal(got["tokens"], ref["tokens"]) and np.array_equal(got["logits"], ref["logits"]), ex
+
+
+def test_prefix_and_resume_invariance(head152):
+    d, h, t = head152
+    _case(cfg=2, invariance="prefix/resume")
+    ds, ts = _slice(d, t, 2, 16)
+    full = run(h, ts, temperature=1, seed=9)
+    pre = run(h, _slice(d, t, 2, 7)[1], temperature=1, seed=9)
+    assert np.array_equal(pre["tokens"], full["tokens"][:, :7])
+    t2 = dict(ts)
+    t2["base"] = ts["base"][:, 7:].contiguous()
+    import torch
+    t2["x0"] = torch.from_numpy(pre["tokens"][:, -1].astype(np.int32)).cuda()
+    rest = run(h, t2, temperature=1, seed=9, step_offset=7)
+    assert np.array_equal(rest["tokens"], full["tokens"][:, 7:])
+    assert np.array_equal(rest["logits"], full["logits"][:, 7:])
+
+
+@pytest.mark.parametrize("reg,lds", [(0, 0), (2, 0), (1, 3), (3, 1)])
+def test_residency_splits_full_size_bitwise(reg, lds):
+    d = cached_inputs(1)
+    _case(cfg=1, reg=reg, lds=lds)
+    h, t = make_head(d, resident_tiles=reg, lds_tiles=lds)
+    p = h.plan(1)
+    assert p["reg_tiles"] <= reg and p["lds_tiles"] <= lds
+    assert_exact(run(h, t), oracle_walk(d), f"reg={reg} lds={lds}")
+    h.close()
+
+
+def test_cooperative_launch_identical():
+    d = cached_inputs(0)
+    _case(cfg=0, cooperative=1)
+    h, t = make_head(d, cooperative=True)
+    assert_exact(run(h, t, temperature=1, seed=2), oracle_walk(d, temperature=1, seed=2), "cooperative")
+    h.close()
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_config3_bf16_tolerance(B):
+    d = cached_inputs(3, B=16)
+    _case(cfg=3, B=B)
+    ds = dict(d)
+    ds["base"], ds["x0"] = d["base"][:B], d["x0"][:B]
+    h, t = make_head(d)
+    p = h.plan(B)
+    assert p["stream_tiles"] > 0                  # 248k bf16 is partially resident
+    ts = dict(t)
+    ts["base"], ts["x0"] = t["base"][:B].contiguous(), t["x0"][:B].contiguous()
+    got = run(h, ts)
+    ref = oracle_walk(ds, keep_z=True)
+    acc = assert_bf16_close(got, ref, f"bf16 B={B}")
+    print("accepted near-tie token mismatches:", acc, flush=True)
+    h.close()
+
+
+def test_bf16_small_tolerance_all_modes():
+    d = datagen.make_inputs(9001, 256, 3, 6, wtype="bf16", seed=21)
+    _case(bf16="small")
+    h, t = make_head(d)
+    ref = oracle_walk(d, keep_z=True)
+    res = run(h, t)
+    assert_bf16_close(res, ref, "bf16 small")
+    for ex in ("stream", "stepwise"):
+        got = run(h, t, exec=ex)
+        # fp32 accumulation order is fixed per tile, so all modes agree bitwise
+        assert np.array_equal(got["logits"], res["logits"]) and np.array_equal(got["tokens"], res["tokens"]), ex
+    h.close()
+
+
+def test_config4_recurrent_full_size_exact():
+    d = cached_inputs(4)
+    _case(cfg=4)
+    h, t = make_head(d)
+    assert_exact(run(h, t), oracle_walk(d), "recurrent 152k")
+    h.close()
+
+
+@pytest.mark.parametrize("V", [1, 15, 16, 33])
+def test_tiny_vocab(V):
+    d = datagen.make_inputs(V, 256, 2, 3, seed=40 + V)
+    _case(V=V)
+    h, t = make_head(d)
+    for T in (0, 1):
+        assert_exact(run(h, t, temperature=T, seed=1), oracle_walk(d, temperature=T, seed=1), f"V={V} T={T}")
+    h.close()
+
+
+def test_max_batch_and_steps():
+    d = datagen.make_inputs(3000, 256, 16, 64, seed=50)
+    _case(B=16, gamma=64)
+    h, t = make_head(d)
+    assert_exact(run(h, t, temperature=1, seed=3), oracle_walk(d, temperature=1, seed=3), "B=16 gamma=64")
+    h.close()
+
+
+def test_last_row_start_and_reuse_across_walks():
+    d = datagen.make_inputs(4097, 256, 2, 5, seed=51)
+    d["x0"][:] = [4096, 0]
+    _case(x0="edges")
+    h, t = make_head(d)
+    ref = oracle_walk(d)
+    for _ in range(3):   # the control block alternates parities walk after walk
+        assert_exact(run(h, t), ref, "reuse")
+    h.close()
