@@ -65,7 +65,8 @@ typedef struct wts_create_params {
   int32_t r;              /* rank; only 256 is built                           */
   int32_t head;           /* WTS_HEAD_*                                        */
   int32_t wtype;          /* WTS_W_*                                           */
-  const void* W;          /* device, [V][r] row-major: int8, or bf16 bits      */
+  const void* W;          /* device, [V][r] row-major: int8, or bf16 bits;
+                             W, E and A 16-byte aligned                       */
   const float* w_scale;   /* device, [V] fp32 per-row scale (int8 only)        */
   const float* E;         /* device, [V][r] fp32 embedding rows                */
   const uint16_t* A;      /* device, [r][r] bf16 bits (recurrent only)         */
@@ -138,9 +139,11 @@ void wts_destroy(wts_ctx* ctx);
  * last clear (WTS_OK if none).  clear != 0 resets the latch. */
 wts_status wts_get_error(wts_ctx* ctx, int clear);
 
-/* Residency a walk of B batch rows under `exec` uses (B selects the batch
- * bucket 1, 2, 4, 8 or 16; larger buckets keep fewer tiles in registers). */
-wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, wts_plan* out);
+/* Residency a walk of B batch rows under `exec` and `temperature` uses (B
+ * selects the batch bucket 1, 2, 4, 8 or 16; larger buckets keep fewer tiles
+ * in registers; T=1 Markov walks keep the next step's noise in LDS, which can
+ * leave room for fewer LDS tiles). */
+wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t temperature, wts_plan* out);
 
 /* Static description of a status code. */
 const char* wts_status_string(wts_status s);

@@ -25,9 +25,10 @@ the design notes):
   * selection is on the returned bf16 logit widened to binary32 (T=0), or on
     fp32(logit + g) with the Gumbel noise g of ``oracle.philox`` (T=1);
     the largest score wins, ties go to the lowest index, -0 equals +0.
-  * recurrent pre-activation: acc_j = sum over k ascending of
-    fp32(fp32(A[j,k]) * h[k]) (binary32 adds, in order), pre = (acc_j +
-    E[x][j]) + c[j], h_j = tanh_p(pre).
+  * recurrent pre-activation: the sum acc_j = sum_k fp32(fp32(A[j,k]) h[k])
+    is taken in binary32 as eight partial sums s_i over k = i, i+8, i+16, ...
+    (each in ascending k), combined as ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7));
+    pre = (acc_j + E[x][j]) + c[j], h_j = tanh_p(pre).
 """
 import numpy as np
 
@@ -96,11 +97,16 @@ def project_bf16(Wb_f64, u_bits):
 
 
 def recurrent_update(A_f32, h, e_row, c):
-    """h_new = tanh_p((sum_k A[:,k] h[k]) + e_row + c), sums in ascending k."""
+    """h_new = tanh_p((sum_k A[:,k] h[k]) + e_row + c).
+
+    The binary32 sum runs as eight interleaved partial sums (k mod 8, each
+    ascending) combined in a fixed pairwise tree.
+    """
     r = h.shape[-1]
-    acc = np.zeros(A_f32.shape[0], dtype=np.float32)
+    s = [np.zeros(A_f32.shape[0], dtype=np.float32) for _ in range(8)]
     for k in range(r):
-        acc = acc + A_f32[:, k] * h[k]
+        s[k % 8] = s[k % 8] + A_f32[:, k] * h[k]
+    acc = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]))
     pre = (acc + np.asarray(e_row, dtype=np.float32)) + np.asarray(c, dtype=np.float32)
     return tanh_p(pre)
 

@@ -52,9 +52,9 @@ class Head:
         _check(_abi.lib().wts_create(ctypes.byref(p), ctypes.byref(h)), "wts_create")
         self._h = h
 
-    def plan(self, B=1, exec="resident"):
+    def plan(self, B=1, exec="resident", temperature=0):
         p = _abi.Plan()
-        _check(_abi.lib().wts_get_plan(self._h, B, EXEC[exec], ctypes.byref(p)), "wts_get_plan")
+        _check(_abi.lib().wts_get_plan(self._h, B, EXEC[exec], temperature, ctypes.byref(p)), "wts_get_plan")
         return p.as_dict()
 
     def walk(self, base, x0, *, h0=None, temperature=0, seed=0, step_offset=0, logits=False,

@@ -71,7 +71,7 @@ def load(path=LIB_PATH):
     lib.wts_destroy.restype = None
     lib.wts_get_error.argtypes = [c_void_p, ctypes.c_int]
     lib.wts_get_error.restype = ctypes.c_int
-    lib.wts_get_plan.argtypes = [c_void_p, c_int32, c_int32, P(Plan)]
+    lib.wts_get_plan.argtypes = [c_void_p, c_int32, c_int32, c_int32, P(Plan)]
     lib.wts_get_plan.restype = ctypes.c_int
     lib.wts_status_string.argtypes = [ctypes.c_int]
     lib.wts_status_string.restype = ctypes.c_char_p

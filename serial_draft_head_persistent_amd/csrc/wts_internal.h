@@ -26,11 +26,20 @@ constexpr int kTileBytesBF = kTileRows * kR * 2;   // 8 KiB
 // LDS of the persistent kernel: scratch for reductions and the latent, then
 // W tiles.  Asking for more than half of the 160 KiB also pins one workgroup
 // per compute unit.
-constexpr int kLdsScratch = 16384;
 constexpr int kLdsMax = 163840;
 
 constexpr int kHeadMarkov = 0;
 constexpr int kHeadRecurrent = 1;
+
+// Int8 Markov walks of one batch row stage the embedding rows of the
+// exchange's candidates (the group maxima) in LDS while the exchange runs.
+constexpr bool stage_candidates(int head, int wtype, int BB) {
+  return head == kHeadMarkov && wtype == 0 && BB == 1;
+}
+// LDS bytes in front of the LDS-resident W tiles.
+constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
+  return head == kHeadRecurrent ? 32768 + kR * kR * 2 : stage_candidates(head, wtype, BB) ? 20480 : 2048;
+}
 
 constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most
 constexpr int kGroups = 16;     // first level of the cross-workgroup selection
@@ -67,6 +76,8 @@ struct WalkArgs {
   int head;
   int reg_tiles;           // per wave, in registers
   int lds_tiles;           // per wave, in LDS
+  int noise_off;           // T=1 persistent Markov walks: LDS offset of the noise rows, else 0
+  int noise_stride;        // floats per batch row in that buffer (>= rows of a workgroup)
   // of this walk
   int B;
   int gamma;

@@ -287,11 +287,16 @@ constexpr int kOffRed = 0;                       // u64 [kWaves][kMaxB]
 constexpr int kOffX = kOffRed + 8 * kWaves * kMaxB;   // int [kMaxB]
 constexpr int kOffShi = kOffX + 4 * kMaxB;        // float [kMaxB]
 constexpr int kOffFlag = kOffShi + 4 * kMaxB;     // int
+constexpr int kOffDone = kOffFlag + 8;           // int: step + 1 whose exchange finished
+constexpr int kOffWin = kOffDone + 8;            // int [kMaxB]: staged row holding the winner
+constexpr int kOffZero = 1280;                   // 256 zero bytes (A-operand source of other slots)
+constexpr int kOffCand = 1536;                   // u64 [kGroups][2]: group maxima seen so far
+constexpr int kOffRows = 2048;                   // [kGroups * 2][512]: staged candidate rows (hi | lo)
+constexpr int kRowBytes = 512;
+constexpr int kOffShs = kOffRows + kGroups * 2 * kRowBytes;  // float [kGroups * 2]: their s_hi
 constexpr int kOffLat = 2048;                     // int8 [kMaxB][2][256] or bf16 [kMaxB][256]
 constexpr int kOffH = kOffLat + kMaxB * 512;       // float [kMaxB][256]
-constexpr int kScratchMarkov = 2048;
-constexpr int kScratchRec = kOffH + kMaxB * kR * 4;  // 26624
-constexpr int kOffAt = 32768;                      // recurrent: A^T bf16 [256][256]
+constexpr int kOffAt = 32768;                      // recurrent: A bf16 as [k/8][256 j][8]
 
 
 __device__ __forceinline__ v4i mma(const v4i& a, const v4i& b, const v4i& c) {
@@ -438,17 +443,42 @@ __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, B
   }
 }
 
+// Same A operands as load_latent, from the candidate rows staged in LDS:
+// the own slot reads the winner's staged row, the other slots the LDS zeros.
+template <int WT, int BB>
+__device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Roles<WT, BB>& ro, const char* lds,
+                                                   v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH]) {
+  using Gm = Geo<WT, BB>;
+#pragma unroll
+  for (int m = 0; m < Gm::NM; ++m) {
+    const int b = ro.arow_b(m);
+    const bool ok = b < a.B;
+    const int slot = ok ? ((const int*)(lds + kOffWin))[b] : 0;
+    const char* src = lds + kOffRows + slot * kRowBytes + ro.arow_hl(m) * 256 + ro.q * 16;
+    const char* zero = lds + kOffZero;
+#pragma unroll
+    for (int s = 0; s < Gm::S; ++s) {
+      const char* p = (ok && ro.aslot == s) ? src : zero;
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = *(const v4i*)(p + c * 64);
+    }
+  }
+}
+
 // Fig. 7 epilogue for the result entries of one M block, then the local
 // selection (Fig. 8 step 1): logit = bf16(((acc_hi s_hi + acc_lo s_lo) s_w) +
 // base) for int8 W, bf16(acc + base) for bf16 W; score = logit (T=0) or
 // logit + Gumbel noise (T=1); keep the largest key per batch entry.
 // Branch-free: lanes without a valid (row, batch) pair contribute key 0.
-template <int WT, int BB, int TEMP>
+// With NZ, T=1 noise comes from LDS (computed one step ahead):
+// noise[b * a.noise_stride + (v - row0)], row0 = the workgroup's first row.
+template <int WT, int BB, int TEMP, bool NZ>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                          const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
                                          float sw, const uint32_t (&bv)[Geo<WT, BB>::NE],
                                          const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
-                                         typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+                                         typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                         const float* noise, int row0) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
@@ -471,7 +501,10 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
     if (TEMP == 0) {
       k = (ord16(lg) << 16) | lrow;
     } else {
-      const float sc = bf16_f32(lg) + gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
+      // lanes without a valid pair read the buffer's first element
+      const float g = NZ ? noise[okb ? b * a.noise_stride + (v - row0) : 0]
+                         : gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
+      const float sc = bf16_f32(lg) + g;
       k = ((unsigned long long)ord32(__float_as_uint(sc)) << 16) | lrow;
     }
     best[m][e] = kmax(best[m][e], okb ? k : (typename LKey<TEMP>::T)0);
@@ -525,13 +558,15 @@ __device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB
 
 // Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), one tile of
 // prefetch.  `cur` holds tile i0 of this step, loaded before the step began.
-template <int WT, int BB, int TEMP, int NWV>
+template <int WT, int BB, int TEMP, int NWV, bool NZ>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
                                              TileBuf<WT, BB> cur,
                                              const v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH],
                                              const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
-                                             typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE]) {
+                                             typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                             const float* noise) {
+  const int row0 = tb * kTileRows;
   using Gm = Geo<WT, BB>;
   using AT = typename AccT<WT>::T;
   for (int i = i0; i < nw; ++i) {
@@ -543,10 +578,14 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
     const uint32_t lrow = 0xFFFFu - (uint32_t)((tile - tb) * kTileRows + ro.n);
 #pragma unroll
     for (int m = 0; m < Gm::NM; ++m) {
-      AT acc = {0, 0, 0, 0};
+      AT acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][0][c], cur.w[c], acc);
-      epilogue<WT, BB, TEMP>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best);
+      for (int c = 0; c < Gm::CH; ++c) {
+        if (WT == 0 && (c & 1)) acc2 = mma(Aop[m][0][c], cur.w[c], acc2);
+        else acc = mma(Aop[m][0][c], cur.w[c], acc);
+      }
+      if (WT == 0) acc = acc + acc2;
+      epilogue<WT, BB, TEMP, NZ>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, noise, row0);
     }
     if (i + 1 < nw) cur = nxt;
   }
@@ -618,9 +657,9 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
 // round-robin dispatch -- and takes the overall maximum.  The keys carry the token, so no other data has to be made
 // visible: relaxed device-scope loads and stores suffice.  Returns false if
 // the watchdog expired.  On return, lanes b < B hold the winning key of row b.
-template <int BB>
+template <int BB, bool CAND>
 __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsigned long long key,
-                                         long long timeout, unsigned long long* winner) {
+                                         long long timeout, unsigned long long* winner, char* lds) {
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x, G = gridDim.x;
   const unsigned long long want = (unsigned long long)(t + 1);
@@ -670,8 +709,12 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
       const int x = q / BB, b = q % BB;
       if (b < B) {
         const unsigned long long v = ld_agent(&L2[((g % kCopies) * kGroups + x) * kMaxB + b]);
-        ok = ok && (v >> kTagShift) == want;
+        const bool here = (v >> kTagShift) == want;
+        ok = ok && here;
         best = umax64(best, v);
+        if (CAND && here)  // let wave 1 start staging this candidate's row
+          __hip_atomic_store((unsigned long long*)(lds + kOffCand) + q, v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     if (__all(ok)) break;
@@ -680,7 +723,76 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
 #pragma unroll
   for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
   *winner = best & kKeyMask;
+  if (CAND && lane == 0)
+    __hip_atomic_store((int*)(lds + kOffDone), ok_all ? t + 1 : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return ok_all;
+}
+
+// Wave 1 during the exchange of step t (int8 Markov, B <= 2): as wave 0
+// publishes group maxima in LDS, copy each candidate's embedding row (hi | lo)
+// and its s_hi from memory straight into LDS (global_load_lds, no registers,
+// nothing waits for it inside the loop).  When the exchange is done, record
+// which staged row holds the winner of each batch row (the largest candidate
+// key) and wait for the copies.  The next step builds its latent from LDS.
+template <int BB>
+__device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, long long timeout) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int lane = threadIdx.x & 63;
+  const int ngr = gridDim.x < kGroups ? gridDim.x : kGroups;
+  const unsigned long long want = (unsigned long long)(t + 1);
+  const bool mine = lane < ngr * BB && (lane % BB) < a.B;  // lane = candidate (group lane/BB, row lane%BB)
+  unsigned long long* cand = (unsigned long long*)(lds + kOffCand);
+  unsigned long long seen = 0ull;  // wave-uniform bit set of candidates looked at
+  // Only a candidate larger than every earlier one of its batch row can win,
+  // so only those rows are copied; the last copied row of each batch row is
+  // the winner once the exchange is complete.
+  unsigned long long bestk[BB];
+  int bestc[BB];
+#pragma unroll
+  for (int b = 0; b < BB; ++b) {
+    bestk[b] = 0ull;
+    bestc[b] = b;
+  }
+  auto stage_new = [&]() {
+    const unsigned long long k =
+        mine ? __hip_atomic_load(cand + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
+    unsigned long long todo = __ballot(mine && (k >> kTagShift) == want) & ~seen;
+    seen |= todo;
+    while (todo) {
+      const int c = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const unsigned long long kc = readlane(k, c);
+      const int b = c % BB;
+      bool better = false;
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb)
+        if (bb == b && kc > bestk[bb]) {
+          bestk[bb] = kc;
+          bestc[bb] = c;
+          better = true;
+        }
+      const int v = key_token(kc & kKeyMask);
+      if (!better || v < 0 || v >= a.V) continue;
+      if (lane < 32)
+        __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
+                                         (lds_void*)(lds + kOffRows + c * kRowBytes), 16, 0, 0);
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + c * 4), 4, 0, 0);
+    }
+  };
+  const long long t0 = wall_clock64();
+  while (true) {
+    const int dn = __hip_atomic_load((int*)(lds + kOffDone), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    stage_new();
+    if (dn == t + 1 || dn == -1) break;
+    if (wall_clock64() - t0 > timeout) break;
+  }
+  stage_new();  // candidates published in the last poll
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < BB; ++b) ((int*)(lds + kOffWin))[b] = bestc[b];
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the LDS copies are complete before the workgroup barrier
 }
 
 // Recurrent head, first half of a step (Fig. 13): h_{t+1} = tanh(A h_t +
@@ -721,31 +833,79 @@ __device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, co
   __syncthreads();
 }
 
-// Recurrent head: racc[b] = sum_k A[j][k] h[b][k], k ascending, one binary32
-// product and one binary32 add per term; A^T (bf16) and h live in LDS.
+// Recurrent head: racc[b] = sum_k A[j][k] h[b][k] in binary32 as eight
+// interleaved partial sums (k mod 8, ascending k in each) combined as
+// ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)): eight independent add chains per
+// thread.  A lives in LDS as [k/8][j][8] bf16, so thread j reads the eight
+// weights of a k-block with one 16-byte load; h is read as a broadcast.
 template <int BB>
 __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, const char* lds, float (&racc)[BB]) {
   if (tid < kThreads - kR) return;
   const int j = tid - (kThreads - kR);
-  const uint16_t* At = (const uint16_t*)(lds + kOffAt);
+  const uint4* A8 = (const uint4*)(lds + kOffAt);
   const float* h = (const float*)(lds + kOffH);
 #pragma unroll
-  for (int b = 0; b < BB; ++b) racc[b] = 0.0f;
-  for (int k = 0; k < kR; k += 4) {
-    float av[4];
+  for (int b = 0; b < BB; ++b) {
+    if (b >= a.B) {
+      racc[b] = 0.0f;
+      continue;
+    }
+    float ps[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) av[u] = bf16_f32(At[(k + u) * kR + j]);
+    for (int i = 0; i < 8; ++i) ps[i] = 0.0f;
+#pragma unroll 4
+    for (int kb = 0; kb < kR / 8; ++kb) {
+      const uint4 w8 = A8[kb * kR + j];
+      const float4 h0 = *(const float4*)(h + b * kR + kb * 8);
+      const float4 h1 = *(const float4*)(h + b * kR + kb * 8 + 4);
+      ps[0] = ps[0] + __uint_as_float(w8.x << 16) * h0.x;
+      ps[1] = ps[1] + __uint_as_float(w8.x & 0xFFFF0000u) * h0.y;
+      ps[2] = ps[2] + __uint_as_float(w8.y << 16) * h0.z;
+      ps[3] = ps[3] + __uint_as_float(w8.y & 0xFFFF0000u) * h0.w;
+      ps[4] = ps[4] + __uint_as_float(w8.z << 16) * h1.x;
+      ps[5] = ps[5] + __uint_as_float(w8.z & 0xFFFF0000u) * h1.y;
+      ps[6] = ps[6] + __uint_as_float(w8.w << 16) * h1.z;
+      ps[7] = ps[7] + __uint_as_float(w8.w & 0xFFFF0000u) * h1.w;
+    }
+    racc[b] = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+  }
+}
+
+// Gumbel noise of step t for every (batch row, vocabulary row) of this
+// workgroup into LDS: one Philox4x32-10 call per group of four consecutive
+// rows (they share the counter and use its four output words), then
+// g = -log(-log U) per word.  Threads [first, first + count) share the work.
+__device__ __forceinline__ void make_noise(const WalkArgs& a, float* noise, int t, int row0, int rows,
+                                           int first, int count) {
+  const int quads = rows >> 2;
+  const int items = a.B * quads;
+  for (int it = (int)threadIdx.x - first; it < items; it += count) {
+    const int b = it / quads, qd = it - b * quads;
+    const int v0 = row0 + 4 * qd;
+    uint32_t c0 = (uint32_t)v0 >> 2, c1 = (uint32_t)(a.step_offset + t), c2 = (uint32_t)b, c3 = 0u;
+    uint32_t k0 = a.seed_lo, k1 = a.seed_hi;
 #pragma unroll
-    for (int b = 0; b < BB; ++b)
-      if (b < a.B) {
-        const float4 hv = *(const float4*)(h + b * kR + k);
-        float s = racc[b];
-        s = s + av[0] * hv.x;
-        s = s + av[1] * hv.y;
-        s = s + av[2] * hv.z;
-        s = s + av[3] * hv.w;
-        racc[b] = s;
+    for (int r = 0; r < 10; ++r) {
+      if (r) {
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
       }
+      const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+      const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+      const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+      c0 = n0;
+      c1 = lo1;
+      c2 = n2;
+      c3 = lo0;
+    }
+    const uint32_t wv[4] = {c0, c1, c2, c3};
+    float g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float u = (float)(2u * (wv[i] >> 9) + 1u) * 5.9604644775390625e-08f;
+      g[i] = -log_p(-log_p(u));
+    }
+    *(float4*)(noise + b * a.noise_stride + 4 * qd) = make_float4(g[0], g[1], g[2], g[3]);
   }
 }
 
@@ -798,7 +958,9 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   const int nlds = min(nw - nreg, a.lds_tiles);
   Ctrl* ctrl = a.ctrl;
   const int par = a.parity;
-  const int scratch = HEAD == kHeadMarkov ? kScratchMarkov : kOffAt + kR * kR * 2;
+  constexpr bool CAND = stage_candidates(HEAD, WT, BB);
+  constexpr bool NOISE = TEMP && HEAD == kHeadMarkov;  // noise one step ahead in LDS
+  const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
   char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
 
   clear_next_walk(ctrl, par);
@@ -828,8 +990,15 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     gsw[gi] = (WT == 0 && gok[gi]) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
   }
   const int row0 = tb * kTileRows;  // first vocabulary row of this workgroup
+  float* noise_lds = NOISE ? (float*)(lds + a.noise_off) : nullptr;
+  const float* noise = noise_lds;
 
   if (tid == 0) *sflag = 0;
+  if (CAND) {
+    for (int i = tid; i < 64; i += kThreads) ((int*)(lds + kOffZero))[i] = 0;
+    for (int i = tid; i < kGroups * 2; i += kThreads) ((unsigned long long*)(lds + kOffCand))[i] = 0ull;
+    if (tid == 0) *(int*)(lds + kOffDone) = 0;
+  }
   float racc[BB];
   float cj = 0.0f;
   __syncthreads();
@@ -843,12 +1012,17 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     sx[tid] = x;
   }
   if (HEAD == kHeadRecurrent) {
-    uint16_t* At = (uint16_t*)(lds + kOffAt);
-    for (int i = tid; i < kR * kR; i += kThreads) At[(i % kR) * kR + i / kR] = a.A[i];
+    // A[j][k] -> [k/8][j][k%8] (bf16): 16-byte pieces, A is 16-byte aligned
+    uint4* At = (uint4*)(lds + kOffAt);
+    for (int i = tid; i < kR * kR / 8; i += kThreads) {
+      const int j = i / (kR / 8), kb = i % (kR / 8);
+      At[kb * kR + j] = ((const uint4*)a.A)[i];
+    }
     float* h = (float*)(lds + kOffH);
     for (int i = tid; i < a.B * kR; i += kThreads) h[i] = a.h0[i];
     if (tid >= kThreads - kR) cj = a.c[tid - (kThreads - kR)];
   }
+  if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, 0, kThreads);
   __syncthreads();
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
@@ -881,14 +1055,21 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
       for (int e = 0; e < Gm::NE; ++e) {
         const int b = ro.bent(m, e);
         shi[m][e] = 0.0f;
-        if (WT == 0 && b < BB && b < a.B)
-          shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
+        if (WT == 0 && b < BB && b < a.B) {
+          if (CAND && t > 0)
+            shi[m][e] = ((const float*)(lds + kOffShs))[((const int*)(lds + kOffWin))[b]];
+          else
+            shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
+        }
       }
     // first non-register tile of this step: its load overlaps the register tiles' work
     TileBuf<WT, BB> first;
     if (nreg < nw) fetch_tile<WT, BB, kWaves>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i Aop[Gm::NM][Gm::S][Gm::CH];
-    load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
+    if (CAND && t > 0)
+      load_latent_staged<WT, BB>(a, ro, lds, Aop);
+    else
+      load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
     if (a.trace) {
       __builtin_amdgcn_s_waitcnt(0);
       stamp(t, 1);
@@ -905,22 +1086,31 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
       if (gi * Gm::S < nreg) {
 #pragma unroll
         for (int m = 0; m < Gm::NM; ++m) {
-          AT acc = {0, 0, 0, 0};
+          // int8: two independent accumulator chains (even / odd chunks), summed
+          // exactly at the end; bf16 keeps one chain (the fp32 order of every
+          // execution mode is the same: chunk 0..7 per tile).
+          AT acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+          const bool full = (gi + 1) * Gm::S <= nreg;
 #pragma unroll
           for (int s = 0; s < Gm::S; ++s) {
             const int i = gi * Gm::S + s;
-            if (i < Gm::RT && i < nreg) {
+            if (i < Gm::RT && (full || i < nreg)) {
 #pragma unroll
-              for (int c = 0; c < Gm::CH; ++c) acc = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc);
+              for (int c = 0; c < Gm::CH; ++c) {
+                if (WT == 0 && (c & 1)) acc2 = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc2);
+                else acc = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc);
+              }
             }
           }
-          epilogue<WT, BB, TEMP>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0), gok[gi],
-                                 gsw[gi], bnx[gi][m], shi, best);
+          if (WT == 0) acc = acc + acc2;
+          epilogue<WT, BB, TEMP, NOISE>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0), gok[gi],
+                                 gsw[gi], bnx[gi][m], shi, best, noise, row0);
         }
       }
     }
     // LDS-resident and streamed tiles
-    if (nreg < nw) stream_tiles<WT, BB, TEMP, kWaves>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best);
+    if (nreg < nw)
+      stream_tiles<WT, BB, TEMP, kWaves, NOISE>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, noise);
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
@@ -928,7 +1118,11 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
     __syncthreads();
     stamp(t, 2);
-    if (w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP>(a, red, row0, ro.lane, lds + kOffFlag + 4);
+    if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP>(a, red, row0, ro.lane, lds + kOffFlag + 4);
+    if (CAND && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
+    // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
+    if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
+      make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, kThreads - (CAND ? 2 : 1) * 64);
     if (w == 0) {
       const int lane = ro.lane;
       unsigned long long k = 0ull;
@@ -939,7 +1133,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
         k = global_key(lk, row0);
       }
       unsigned long long win;
-      const bool ok = exchange<BB>(ctrl, par, t, a.B, k, a.timeout_ticks, &win);
+      const bool ok = exchange<BB, CAND>(ctrl, par, t, a.B, k, a.timeout_ticks, &win, lds);
       if (!ok && lane == 0) {
         latch_error(ctrl, 5u);
         *sflag = 1;
@@ -1025,7 +1219,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   if (nw > 0) {
     TileBuf<WT, BB> first;
     fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
-    stream_tiles<WT, BB, TEMP, kStepWaves>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best);
+    stream_tiles<WT, BB, TEMP, kStepWaves, false>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best,
+                                           (const float*)nullptr);
   }
   reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
   __syncthreads();

@@ -55,16 +55,28 @@ int batch_bucket(int B) {
 
 int tile_bytes(int wtype) { return wtype == WTS_W_INT8 ? kTileBytesI8 : kTileBytesBF; }
 
-int lds_scratch(int head) { return head == WTS_HEAD_MARKOV ? 2048 : 32768 + kR * kR * 2; }
+
+// Gumbel noise of a T=1 persistent Markov walk is computed one step ahead
+// into LDS (BB rows x the workgroup's vocabulary rows, fp32).
+int noise_floats(const wts_ctx* ctx, int BB, int temperature) {
+  if (!temperature || ctx->head != WTS_HEAD_MARKOV) return 0;
+  const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
+  return per_wg * kTileRows;
+}
 
 // Residency plan for one batch bucket.
-void make_plan(const wts_ctx* ctx, int BB, int exec, wts_plan* p, int* lds_bytes) {
+void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* p, int* lds_bytes,
+               int* noise_off = nullptr, int* noise_stride = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
   const int per_wave = (per_wg + kWaves - 1) / kWaves;
   int reg = std::min(reg_tiles_max(ctx->wtype, BB), per_wave);
   if (ctx->reg_cap >= 0) reg = std::min(reg, ctx->reg_cap);
   const int tb = tile_bytes(ctx->wtype);
-  const int scratch = lds_scratch(ctx->head);
+  const int stride = noise_floats(ctx, BB, temperature);
+  const int noise_bytes = BB * stride * 4;
+  const int scratch = lds_scratch_bytes(ctx->head, ctx->wtype, BB) + noise_bytes;
+  if (noise_off) *noise_off = stride ? lds_scratch_bytes(ctx->head, ctx->wtype, BB) : 0;
+  if (noise_stride) *noise_stride = stride;
   int lds = std::max(0, (kLdsMax - scratch) / (kWaves * tb));
   lds = std::min(lds, per_wave - reg);
   if (ctx->lds_cap >= 0) lds = std::min(lds, ctx->lds_cap);
@@ -142,7 +154,8 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   if (p->max_batch < 1 || p->max_batch > kMaxB) return WTS_ERR_INVALID_ARG;
   if (p->max_steps < 1 || p->max_steps > kMaxSteps) return WTS_ERR_INVALID_ARG;
   if (p->resident_tiles < -1 || p->lds_tiles < -1) return WTS_ERR_INVALID_ARG;
-  if (((uintptr_t)p->W & 15) || ((uintptr_t)p->E & 15)) return WTS_ERR_INVALID_ARG;
+  if (((uintptr_t)p->W & 15) || ((uintptr_t)p->E & 15) || ((uintptr_t)p->A & 15) || ((uintptr_t)p->c & 3))
+    return WTS_ERR_INVALID_ARG;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev) return WTS_ERR_INVALID_ARG;
   DeviceGuard guard(p->device);
@@ -206,11 +219,12 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   return WTS_OK;
 }
 
-wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, wts_plan* out) {
+wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t temperature, wts_plan* out) {
   if (!ctx || !out || B < 1 || B > ctx->max_batch) return WTS_ERR_INVALID_ARG;
   if (exec < WTS_EXEC_RESIDENT || exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
+  if (temperature != 0 && temperature != 1) return WTS_ERR_INVALID_ARG;
   int lds_bytes = 0;
-  make_plan(ctx, batch_bucket(B), exec, out, &lds_bytes);
+  make_plan(ctx, batch_bucket(B), exec, temperature, out, &lds_bytes);
   return WTS_OK;
 }
 
@@ -231,7 +245,8 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   const int BB = batch_bucket(p->B);
   wts_plan plan;
   int lds_bytes = 0;
-  make_plan(ctx, BB, p->exec, &plan, &lds_bytes);
+  int noise_off = 0, noise_stride = 0;
+  make_plan(ctx, BB, p->exec, p->temperature, &plan, &lds_bytes, &noise_off, &noise_stride);
 
   WalkArgs a{};
   a.Wp = ctx->Wp;
@@ -248,6 +263,8 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.head = ctx->head;
   a.reg_tiles = plan.reg_tiles;
   a.lds_tiles = plan.lds_tiles;
+  a.noise_off = noise_off;
+  a.noise_stride = noise_stride;
   a.B = p->B;
   a.gamma = p->gamma;
   a.step_offset = p->step_offset;

@@ -48,9 +48,11 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0):
                 A = bf16_to_f32(d["A"])
                 hn = []
                 for j in range(r):
-                    acc = Fraction(0)
+                    ps = [Fraction(0)] * 8   # eight interleaved partial sums, fixed tree
                     for k in range(r):
-                        acc = rnd32(acc + rnd32(_F(A[j, k]) * _F(h[k])))
+                        ps[k % 8] = rnd32(ps[k % 8] + rnd32(_F(A[j, k]) * _F(h[k])))
+                    acc = rnd32(rnd32(rnd32(ps[0] + ps[1]) + rnd32(ps[2] + ps[3]))
+                                + rnd32(rnd32(ps[4] + ps[5]) + rnd32(ps[6] + ps[7])))
                     pre = rnd32(rnd32(acc + _F(E[x, j])) + _F(d["c"][j]))
                     hn.append(tanh_p(np.float32(float(pre))))
                 h = hn
@@ -78,7 +80,9 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0):
 @pytest.mark.parametrize("head", ["markov", "recurrent"])
 def test_toy_walk_brute_force(temperature, head):
     # Fig. 2 toy shape: V=12, r=4, three steps (two batch rows)
-    d = datagen.make_inputs(12, 4, 2, 3, head=head, seed=11)
+    # recurrent: r=16 so that every one of the eight partial sums has two terms
+    r = 4 if head == "markov" else 16
+    d = datagen.make_inputs(12, r, 2, 3, head=head, seed=11)
     toks, lg = _brute_walk(d, temperature, seed=3)
     o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head=head,
                     A=d["A"], c=d["c"], h0=d["h0"], temperature=temperature, seed=3)
