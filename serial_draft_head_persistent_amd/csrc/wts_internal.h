@@ -9,15 +9,21 @@ namespace wts {
 
 constexpr int kR = 256;           // latent rank the kernels are built for
 constexpr int kTileRows = 16;     // vocabulary rows per W tile (one MFMA N block)
-constexpr int kWaves = 8;         // waves per workgroup of the persistent kernel
+constexpr int kWaves = 8;         // waves per workgroup of the persistent kernel (at most)
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxB = 16;
 constexpr int kMaxSteps = 64;
-// 16-row W tiles a wave of the persistent kernel holds in VGPRs.  Larger
+// Waves per workgroup of the persistent kernel.  bf16 Markov walks use 4
+// waves (one per SIMD): each wave then has the whole 512-entry register file
+// of its SIMD lane (VGPRs + AGPRs) and keeps 8 bf16 tiles (64 KiB per wave)
+// resident; everything else uses 8 waves.
+constexpr int waves_for(int head, int wtype) { return (head == 0 && wtype == 1) ? 4 : 8; }
+// 16-row W tiles a wave of the persistent kernel holds in registers.  Larger
 // batches need more registers for latents and keys, so they keep fewer tiles
 // in registers and more in LDS.
-constexpr int reg_tiles_max(int wtype, int BB) {
-  return wtype == 0 ? (BB <= 2 ? 5 : BB == 4 ? 4 : BB == 8 ? 3 : 2) : 1;
+constexpr int reg_tiles_max(int head, int wtype, int BB) {
+  return wtype == 0 ? (BB <= 2 ? 5 : BB == 4 ? 4 : BB == 8 ? 3 : 2)
+                    : waves_for(head, wtype) == 4 ? (BB == 1 ? 8 : BB == 2 ? 7 : BB <= 8 ? 6 : 5) : 1;
 }
 constexpr int kChunksI8 = 4;      // 16-byte lane chunks per int8 tile (64 k each)
 constexpr int kChunksBF = 8;      // 16-byte lane chunks per bf16 tile (32 k each)

@@ -269,7 +269,7 @@ __global__ void bf16_rows_kernel(const float* __restrict__ E, long long n, uint1
 // Geometry of one (W type, batch bucket).  The A operand carries LPB latent
 // rows per batch row (hi and lo for int8, one for bf16).  With RPS latent
 // rows per slot, S = 16 / RPS tiles share one accumulator.
-template <int WT, int BB>
+template <int WT, int BB, int HD = 0>
 struct Geo {
   static constexpr int LPB = WT == 0 ? 2 : 1;
   static constexpr int ROWS = LPB * BB;
@@ -277,7 +277,7 @@ struct Geo {
   static constexpr int RPS = WT == 0 ? (ROWS <= 4 ? 4 : (ROWS <= 8 ? 8 : 16)) : 16;
   static constexpr int S = 16 / RPS;
   static constexpr int CH = WT == 0 ? kChunksI8 : kChunksBF;
-  static constexpr int RT = reg_tiles_max(WT, BB);
+  static constexpr int RT = reg_tiles_max(HD, WT, BB);
   static constexpr int NG = (RT + S - 1) / S;
   static constexpr int NE = 4 / LPB;  // batch entries per lane and M block
 };
@@ -913,7 +913,7 @@ __device__ __forceinline__ void make_noise(const WalkArgs& a, float* noise, int 
 // workgroup's local winner (one word per 128-byte line).  One of these rows
 // is the next step's latent; reading it now brings it into the device-side
 // cache, so the gather after the exchange does not wait for HBM.
-template <int WT, int HEAD, int TEMP>
+template <int WT, int HEAD, int TEMP, int NW>
 __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned long long* red, int row0,
                                               int lane, char* lds_dummy) {
   constexpr int LINES = HEAD == kHeadMarkov ? (WT == 0 ? 5 : 4) : 8;  // 128-byte lines per row
@@ -922,7 +922,7 @@ __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned 
     const int b = q / LINES, j = q % LINES;
     typename LKey<TEMP>::T lk = 0;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + b]);
+    for (int ww = 0; ww < NW; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + b]);
     const int v = key_token(global_key(lk, row0));
     if (v >= 0 && v < a.V) {
       if (HEAD == kHeadMarkov && WT == 0)
@@ -938,8 +938,10 @@ __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned 
 
 // The whole walk in one cooperative launch: grid = one workgroup per CU.
 template <int WT, int BB, int HEAD, int TEMP>
-__global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
-  using Gm = Geo<WT, BB>;
+__global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkArgs a) {
+  constexpr int NW = waves_for(HEAD, WT);
+  constexpr int NT = NW * 64;
+  using Gm = Geo<WT, BB, HEAD>;
   using AT = typename AccT<WT>::T;
   constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -953,7 +955,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   const int tb = (int)((long long)g * a.tiles / G);
   const int te = (int)((long long)(g + 1) * a.tiles / G);
   const int cnt = te - tb;
-  const int nw = cnt > w ? (cnt - w + kWaves - 1) / kWaves : 0;
+  const int nw = cnt > w ? (cnt - w + NW - 1) / NW : 0;
   const int nreg = min(nw, a.reg_tiles);
   const int nlds = min(nw - nreg, a.lds_tiles);
   Ctrl* ctrl = a.ctrl;
@@ -969,12 +971,12 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   v4i wr[Gm::RT][Gm::CH];
 #pragma unroll
   for (int i = 0; i < Gm::RT; ++i) {
-    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + kWaves * i) * Gm::CH * 64 + ro.lane;
+    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * i) * Gm::CH * 64 + ro.lane;
 #pragma unroll
     for (int c = 0; c < Gm::CH; ++c) wr[i][c] = (i < nreg) ? p[c * 64] : v4i{0, 0, 0, 0};
   }
   for (int i = 0; i < nlds; ++i) {
-    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + kWaves * (nreg + i)) * Gm::CH * 64 + ro.lane;
+    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * (nreg + i)) * Gm::CH * 64 + ro.lane;
 #pragma unroll
     for (int c = 0; c < Gm::CH; ++c) *(v4i*)(ldsw + (size_t)i * TB + c * 1024 + ro.lane * 16) = p[c * 64];
   }
@@ -984,7 +986,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
 #pragma unroll
   for (int gi = 0; gi < Gm::NG; ++gi) {
     const int i = gi * Gm::S + ro.cslot;
-    const int tile = tb + w + kWaves * i;
+    const int tile = tb + w + NW * i;
     gv[gi] = tile * kTileRows + ro.n;
     gok[gi] = i < nreg && gv[gi] < a.V;
     gsw[gi] = (WT == 0 && gok[gi]) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
@@ -995,8 +997,8 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
 
   if (tid == 0) *sflag = 0;
   if (CAND) {
-    for (int i = tid; i < 64; i += kThreads) ((int*)(lds + kOffZero))[i] = 0;
-    for (int i = tid; i < kGroups * 2; i += kThreads) ((unsigned long long*)(lds + kOffCand))[i] = 0ull;
+    for (int i = tid; i < 64; i += NT) ((int*)(lds + kOffZero))[i] = 0;
+    for (int i = tid; i < kGroups * 2; i += NT) ((unsigned long long*)(lds + kOffCand))[i] = 0ull;
     if (tid == 0) *(int*)(lds + kOffDone) = 0;
   }
   float racc[BB];
@@ -1014,15 +1016,15 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   if (HEAD == kHeadRecurrent) {
     // A[j][k] -> [k/8][j][k%8] (bf16): 16-byte pieces, A is 16-byte aligned
     uint4* At = (uint4*)(lds + kOffAt);
-    for (int i = tid; i < kR * kR / 8; i += kThreads) {
+    for (int i = tid; i < kR * kR / 8; i += NT) {
       const int j = i / (kR / 8), kb = i % (kR / 8);
       At[kb * kR + j] = ((const uint4*)a.A)[i];
     }
     float* h = (float*)(lds + kOffH);
-    for (int i = tid; i < a.B * kR; i += kThreads) h[i] = a.h0[i];
+    for (int i = tid; i < a.B * kR; i += NT) h[i] = a.h0[i];
     if (tid >= kThreads - kR) cj = a.c[tid - (kThreads - kR)];
   }
-  if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, 0, kThreads);
+  if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, 0, NT);
   __syncthreads();
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
@@ -1064,7 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
       }
     // first non-register tile of this step: its load overlaps the register tiles' work
     TileBuf<WT, BB> first;
-    if (nreg < nw) fetch_tile<WT, BB, kWaves>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
+    if (nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i Aop[Gm::NM][Gm::S][Gm::CH];
     if (CAND && t > 0)
       load_latent_staged<WT, BB>(a, ro, lds, Aop);
@@ -1110,7 +1112,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     }
     // LDS-resident and streamed tiles
     if (nreg < nw)
-      stream_tiles<WT, BB, TEMP, kWaves, NOISE>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, noise);
+      stream_tiles<WT, BB, TEMP, NW, NOISE>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, noise);
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
@@ -1118,18 +1120,18 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
     reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
     __syncthreads();
     stamp(t, 2);
-    if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP>(a, red, row0, ro.lane, lds + kOffFlag + 4);
+    if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
     if (CAND && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
-      make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, kThreads - (CAND ? 2 : 1) * 64);
+      make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
     if (w == 0) {
       const int lane = ro.lane;
       unsigned long long k = 0ull;
       if (lane < a.B) {
         typename LKey<TEMP>::T lk = 0;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + lane]);
+        for (int ww = 0; ww < NW; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + lane]);
         k = global_key(lk, row0);
       }
       unsigned long long win;
@@ -1157,7 +1159,7 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
   }
   if (HEAD == kHeadRecurrent && g == 0 && a.state) {
     const float* h = (const float*)(lds + kOffH);
-    for (int i = tid; i < a.B * kR; i += kThreads) a.state[i] = h[i];
+    for (int i = tid; i < a.B * kR; i += NT) a.state[i] = h[i];
   }
 }
 
@@ -1281,9 +1283,10 @@ template <int WT, int BB, int HEAD, int TEMP>
 static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   void* args[] = {(void*)&a};
   if (coop)
-    return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads),
+    return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid),
+                                      dim3(waves_for(HEAD, WT) * 64),
                                       args, (unsigned)lds_bytes, s);
-  return hipLaunchKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(kThreads), args,
+  return hipLaunchKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(waves_for(HEAD, WT) * 64), args,
                          (size_t)lds_bytes, s);
 }
 

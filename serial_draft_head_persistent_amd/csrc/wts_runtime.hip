@@ -68,8 +68,9 @@ int noise_floats(const wts_ctx* ctx, int BB, int temperature) {
 void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* p, int* lds_bytes,
                int* noise_off = nullptr, int* noise_stride = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
-  const int per_wave = (per_wg + kWaves - 1) / kWaves;
-  int reg = std::min(reg_tiles_max(ctx->wtype, BB), per_wave);
+  const int NW = waves_for(ctx->head, ctx->wtype);
+  const int per_wave = (per_wg + NW - 1) / NW;
+  int reg = std::min(reg_tiles_max(ctx->head, ctx->wtype, BB), per_wave);
   if (ctx->reg_cap >= 0) reg = std::min(reg, ctx->reg_cap);
   const int tb = tile_bytes(ctx->wtype);
   const int stride = noise_floats(ctx, BB, temperature);
@@ -77,12 +78,12 @@ void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* 
   const int scratch = lds_scratch_bytes(ctx->head, ctx->wtype, BB) + noise_bytes;
   if (noise_off) *noise_off = stride ? lds_scratch_bytes(ctx->head, ctx->wtype, BB) : 0;
   if (noise_stride) *noise_stride = stride;
-  int lds = std::max(0, (kLdsMax - scratch) / (kWaves * tb));
+  int lds = std::max(0, (kLdsMax - scratch) / (NW * tb));
   lds = std::min(lds, per_wave - reg);
   if (ctx->lds_cap >= 0) lds = std::min(lds, ctx->lds_cap);
   if (exec != WTS_EXEC_RESIDENT) reg = lds = 0;
   p->grid = ctx->grid;
-  p->waves = kWaves;
+  p->waves = NW;
   p->tiles = ctx->tiles;
   p->tiles_per_wave = per_wave;
   p->reg_tiles = reg;
@@ -92,8 +93,8 @@ void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* 
   long long res_tiles = 0;
   for (int g = 0; g < ctx->grid; ++g) {
     const int cnt = (int)((long long)(g + 1) * ctx->tiles / ctx->grid) - (int)((long long)g * ctx->tiles / ctx->grid);
-    for (int w = 0; w < kWaves; ++w) {
-      const int nw = cnt > w ? (cnt - w + kWaves - 1) / kWaves : 0;
+    for (int w = 0; w < NW; ++w) {
+      const int nw = cnt > w ? (cnt - w + NW - 1) / NW : 0;
       res_tiles += std::min(nw, reg + lds);
     }
   }
@@ -101,7 +102,7 @@ void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* 
   p->w_bytes = (long long)ctx->V * kR * esz;
   p->resident_bytes = res_tiles * tb;
   p->streamed_bytes = (long long)ctx->tiles * tb - p->resident_bytes;
-  *lds_bytes = std::min(kLdsMax, std::max(scratch + kWaves * lds * tb, 96 * 1024));
+  *lds_bytes = std::min(kLdsMax, std::max(scratch + NW * lds * tb, 96 * 1024));
 }
 
 template <class T>
