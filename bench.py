@@ -185,7 +185,7 @@ def cpu_baseline(d, budget_s=12.0):
         oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], keep_logits=False)
         walks += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or walks >= 50:
+        if el >= budget_s or walks >= 400:
             break
     return {"value": el / walks * 1e6, "unit": "us/walk", "cores": int(threads), "kind": "oracle",
             "sample": f"{walks} complete walks of the headline workload (V=151936, B=1, gamma=16, greedy), "

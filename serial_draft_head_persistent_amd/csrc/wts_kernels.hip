@@ -496,7 +496,9 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
     }
     z = z + bf16_f32(bv[e]);
     const uint32_t lg = bf16_rne(z);
-    if (a.logits && okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
+    if (a.logits != nullptr) {  // uniform: skipped entirely when logits are not requested
+      if (okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
+    }
     typename LKey<TEMP>::T k;
     if (TEMP == 0) {
       k = (ord16(lg) << 16) | lrow;
