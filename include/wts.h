@@ -58,6 +58,13 @@ enum { WTS_W_INT8 = 0, WTS_W_BF16 = 1 };
  * All three compute identical tokens and logits. */
 enum { WTS_EXEC_RESIDENT = 0, WTS_EXEC_STREAM = 1, WTS_EXEC_STEPWISE = 2 };
 
+/* Walk flags.
+ *  FIXED_LATENT: the fixed-latent probe of Fig. 13b.  Every step projects and
+ *            selects with the latent of step 0 (Markov: E[x0]; recurrent:
+ *            h_1); each step's choice is written to tokens_out but does not
+ *            feed back.  It times a step without its state advance. */
+enum { WTS_WALK_FIXED_LATENT = 1 };
+
 typedef struct wts_ctx wts_ctx;
 
 typedef struct wts_create_params {
@@ -99,13 +106,21 @@ typedef struct wts_walk_params {
   uint16_t* logits_out;   /* device, [B][gamma][V] bf16 bits, or NULL          */
   float* state_out;       /* device, [B][r] fp32 final state, or NULL          */
   int32_t exec;           /* WTS_EXEC_*                                        */
-  int32_t reserved;       /* must be 0                                         */
+  int32_t flags;          /* 0 or WTS_WALK_FIXED_LATENT; other bits invalid    */
   void* stream;           /* hipStream_t (NULL = default stream)               */
   int64_t* trace_out;     /* device, [gamma][grid][4] int64, or NULL.  Persistent
                              executions only: per step and workgroup, wall-clock
                              stamps (100 MHz ticks) at step start, latent
                              loaded, local winner ready, common winner known.
                              Per-step breakdown in the manner of Fig. 13b.     */
+  float* lse_out;         /* device, [B][gamma] fp32, or NULL: per step, the
+                             log normaliser ln sum_v exp(l_v) of that step's
+                             bf16 logits l.  A T=1 walk samples its token from
+                             q(v) = exp(l_v - lse) (Gumbel-max, Fig. 10), so
+                             log q of the drafted token is l[x_t] - lse: what a
+                             lossless verifier needs, without a second pass
+                             over the logits.  Accumulated in fp32 in the
+                             kernel (online max and rescaled sum).            */
 } wts_walk_params;
 
 typedef struct wts_plan {

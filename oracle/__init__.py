@@ -5,7 +5,7 @@ Decoding" (arXiv 2611.00506): abstract, Fig. 2 (serial refinement through one
 shared vocabulary projection), Fig. 7 (two int8 vectors for the latent, scaled
 results summed, base logits added, one rounding to bf16), Fig. 8 (selection of
 one common winner across all workers), Fig. 10 (T=0 and T=1), Fig. 13
-(Markov and recurrent heads).
+(Markov and recurrent heads; the fixed-latent probe of Fig. 13b).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -23,5 +23,5 @@ from .quant import quant_hilo  # noqa: F401
 from .philox import philox4x32_10, uniform24, gumbel_noise  # noqa: F401
 from .walk import (  # noqa: F401
     order_key, select_token, project_int8, epilogue_int8, project_bf16,
-    recurrent_update, walk,
+    recurrent_update, log_normaliser, walk,
 )

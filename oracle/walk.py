@@ -29,7 +29,16 @@ the design notes):
     is taken in binary32 as eight partial sums s_i over k = i, i+8, i+16, ...
     (each in ascending k), combined as ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7));
     pre = (acc_j + E[x][j]) + c[j], h_j = tanh_p(pre).
+  * fixed-latent probe (Fig. 13b): every step projects and selects with the
+    latent of step 0 (Markov: E[x_0]; recurrent: h_1); the chosen tokens are
+    emitted but do not feed back.
+  * per-step normaliser of the draft distribution: at T=1 the Gumbel-max
+    choice samples q(v) = exp(l_v) / sum_u exp(l_u) over the returned bf16
+    logits l (widened exactly); its log normaliser lse = ln sum_u exp(l_u) is
+    an optional output, taken here in float64.
 """
+import math
+
 import numpy as np
 
 from .fp import bf16_rne, bf16_to_f32, tanh_p
@@ -111,9 +120,22 @@ def recurrent_update(A_f32, h, e_row, c):
     return tanh_p(pre)
 
 
+def log_normaliser(logit_bits):
+    """ln sum_v exp(l_v) of one step's bf16 logits, in float64.
+
+    The log normaliser of the draft distribution q(v) = exp(l_v - lse) that a
+    Gumbel-max walk at T=1 samples from (Fig. 10, T=1).  Definition, with the
+    largest logit factored out so no term overflows; math.fsum adds the terms
+    with a single final rounding.
+    """
+    l = bf16_to_f32(np.asarray(logit_bits, dtype=np.uint16)).astype(np.float64)
+    m = float(l.max())
+    return m + math.log(math.fsum(np.exp(l - m).tolist()))
+
+
 def walk(W, E, base, x0, *, wtype="int8", s_w=None, head="markov", A=None,
          c=None, h0=None, temperature=0, seed=0, step_offset=0,
-         keep_logits=True, keep_z=False):
+         keep_logits=True, keep_z=False, keep_lse=False, fixed_latent=False):
     """Run the walk for every batch row.
 
     W: int8 [V, r] (wtype 'int8', with s_w float32 [V]) or bf16 bits uint16
@@ -121,9 +143,13 @@ def walk(W, E, base, x0, *, wtype="int8", s_w=None, head="markov", A=None,
     x0: int [B].  Recurrent head: A bf16 bits [r, r], c float32 [r], h0
     float32 [B, r].  temperature 0 (greedy) or 1 (Gumbel-max).
 
+    fixed_latent: the probe of Fig. 13b -- every step uses the latent of step
+    0 and the tokens do not feed back.
+
     Returns dict with 'tokens' int32 [B, gamma], 'logits' uint16 [B, gamma, V]
     (if keep_logits), 'z' float32 [B, gamma, V] (if keep_z; the value that
-    is rounded to the logit), 'state' float32 [B, r] (recurrent) .
+    is rounded to the logit), 'lse' float64 [B, gamma] (if keep_lse; the log
+    normaliser of each step's logits), 'state' float32 [B, r] (recurrent).
     """
     if temperature not in (0, 1):
         raise ValueError("temperature must be 0 or 1")
@@ -141,11 +167,12 @@ def walk(W, E, base, x0, *, wtype="int8", s_w=None, head="markov", A=None,
     tokens = np.zeros((B, gamma), dtype=np.int32)
     logits = np.zeros((B, gamma, V), dtype=np.uint16) if keep_logits else None
     zs = np.zeros((B, gamma, V), dtype=np.float32) if keep_z else None
+    lse = np.zeros((B, gamma), dtype=np.float64) if keep_lse else None
     vidx = np.arange(V, dtype=np.int64)
     for t in range(gamma):
         if head == "markov":
             lat = E[x_prev]                                   # [B, r]
-        else:
+        elif t == 0 or not fixed_latent:
             for b in range(B):
                 h[b] = recurrent_update(A32, h[b], E[x_prev[b]], c)
             lat = h
@@ -168,7 +195,10 @@ def walk(W, E, base, x0, *, wtype="int8", s_w=None, head="markov", A=None,
                 logits[b, t] = lg
             if keep_z:
                 zs[b, t] = z
-        x_prev = tokens[:, t].astype(np.int64)
-    out = {"tokens": tokens, "logits": logits, "z": zs}
+            if keep_lse:
+                lse[b, t] = log_normaliser(lg)
+        if not fixed_latent:
+            x_prev = tokens[:, t].astype(np.int64)
+    out = {"tokens": tokens, "logits": logits, "z": zs, "lse": lse}
     out["state"] = h if head == "recurrent" else None
     return out

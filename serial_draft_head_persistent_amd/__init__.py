@@ -58,13 +58,16 @@ class Head:
         return p.as_dict()
 
     def walk(self, base, x0, *, h0=None, temperature=0, seed=0, step_offset=0, logits=False,
-             state=False, exec="resident", stream=None, out=None, trace=False):
+             state=False, lse=False, exec="resident", fixed_latent=False, stream=None, out=None,
+             trace=False):
         """Enqueue one walk.  base: bf16 [B, gamma, V]; x0: int32 [B].
 
         Returns a dict of output tensors (tokens int32 [B, gamma]; logits bf16
-        [B, gamma, V], state float32 [B, 256] and trace int64 [gamma, grid, 4]
-        when asked for).  Pass `out` (a dict from an earlier call) to reuse its
-        buffers.
+        [B, gamma, V], state float32 [B, 256], lse float32 [B, gamma] (log
+        normaliser of each step's logits) and trace int64 [gamma, grid, 4]
+        when asked for).  fixed_latent runs the fixed-latent probe (every step
+        uses the latent of step 0).  Pass `out` (a dict from an earlier call)
+        to reuse its buffers.
         """
         torch = self._torch
         B, gamma, V = base.shape
@@ -77,12 +80,16 @@ class Head:
             if trace:
                 out["trace"] = torch.zeros((gamma, self.plan(B)["grid"], 4), dtype=torch.int64,
                                            device=self.device)
+            if lse:
+                out["lse"] = torch.empty((B, gamma), dtype=torch.float32, device=self.device)
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         p = _abi.WalkParams(B=B, gamma=gamma, step_offset=step_offset, temperature=temperature,
                             seed=seed, base=_ptr(base), x0=_ptr(x0), h0=_ptr(h0),
                             tokens_out=_ptr(out["tokens"]), logits_out=_ptr(out.get("logits")),
-                            state_out=_ptr(out.get("state")), exec=EXEC[exec], reserved=0,
-                            stream=ctypes.c_void_p(s.cuda_stream), trace_out=_ptr(out.get("trace")))
+                            state_out=_ptr(out.get("state")), exec=EXEC[exec],
+                            flags=_abi.WALK_FIXED_LATENT if fixed_latent else 0,
+                            stream=ctypes.c_void_p(s.cuda_stream), trace_out=_ptr(out.get("trace")),
+                            lse_out=_ptr(out.get("lse")))
         _check(_abi.lib().wts_walk(self._h, ctypes.byref(p)), "wts_walk")
         return out
 

@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "WTS_OK", 1: "WTS_ERR_INVALID_ARG", 2: "WTS_ERR_UNSUPPORTED",
 HEAD = {"markov": 0, "recurrent": 1}
 WTYPE = {"int8": 0, "bf16": 1}
 EXEC = {"resident": 0, "stream": 1, "stepwise": 2}
+WALK_FIXED_LATENT = 1
 
 EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string"]
 
@@ -33,7 +34,8 @@ class WalkParams(ctypes.Structure):
     _fields_ = [("B", c_int32), ("gamma", c_int32), ("step_offset", c_int32), ("temperature", c_int32),
                 ("seed", c_uint64), ("base", c_void_p), ("x0", c_void_p), ("h0", c_void_p),
                 ("tokens_out", c_void_p), ("logits_out", c_void_p), ("state_out", c_void_p),
-                ("exec", c_int32), ("reserved", c_int32), ("stream", c_void_p), ("trace_out", c_void_p)]
+                ("exec", c_int32), ("flags", c_int32), ("stream", c_void_p), ("trace_out", c_void_p),
+                ("lse_out", c_void_p)]
 
 
 class Plan(ctypes.Structure):

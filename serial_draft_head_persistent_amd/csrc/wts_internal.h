@@ -44,7 +44,12 @@ constexpr bool stage_candidates(int head, int wtype, int BB) {
 }
 // LDS bytes in front of the LDS-resident W tiles.
 constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
-  return head == kHeadRecurrent ? 32768 + kR * kR * 2 : stage_candidates(head, wtype, BB) ? 20480 : 2048;
+  return head == kHeadRecurrent ? 32768 + kR * kR * 2 : stage_candidates(head, wtype, BB) ? 20480 : 3072;
+}
+// LDS offset of the per-wave log-sum-exp pairs (float2 [kWaves][kMaxB]), in
+// a part of the scratch that nothing else of that kernel uses.
+constexpr int lse_lds_offset(int head, int wtype, int BB) {
+  return head == kHeadRecurrent ? 26624 : stage_candidates(head, wtype, BB) ? 18688 : 2048;
 }
 
 constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most
@@ -63,7 +68,8 @@ struct Ctrl {
   // step-wise walk: device-scope max per (step, batch row, sub-slot)
   unsigned long long ss[2][kMaxSteps][kMaxB][kSub];
   unsigned int err;                               // latched wts_status
-  unsigned int pad[63];
+  unsigned int lse_done[2];                       // per walk parity: workgroups done with their partials
+  unsigned int pad[61];
 };
 
 struct WalkArgs {
@@ -101,6 +107,9 @@ struct WalkArgs {
   float* state;
   long long* trace;        // [gamma][grid][4] phase stamps or null
   long long timeout_ticks; // watchdog, in s_memrealtime ticks (100 MHz)
+  int fixed_latent;        // fixed-latent probe: the latent of step 0 at every step
+  float* lse;              // [B][gamma] log normaliser per step, or null
+  float* lse_part;         // [B][gamma][grid] (max, sum) pairs of the workgroups (scratch)
 };
 
 // Launchers (wts_kernels.hip).  Each returns the HIP error of its launch.
@@ -112,7 +121,7 @@ hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s);
 hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes,
                        bool cooperative, hipStream_t s);
 hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s);
-hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
+hipError_t launch_finish(const WalkArgs& a, int grid, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);
 
 }  // namespace wts

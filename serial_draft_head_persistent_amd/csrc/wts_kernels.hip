@@ -465,6 +465,52 @@ __device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Role
   }
 }
 
+// ---- per-step log normaliser of the logits (optional output) ----
+// ln sum_v exp(l_v) is accumulated as (max, sum) pairs in base 2: the pair
+// (m, s) stands for s * 2^m.  Each lane folds its logits into running pairs
+// (one per result entry), the pairs are merged across lanes, waves and
+// workgroups, and the merged pair of each (row, step) becomes (m + log2 s) ln 2.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2f = 0.69314718055994531f;
+constexpr float kLseNone = -3.0e38f;  // max of an empty pair; 2^(kLseNone - m) is 0
+
+struct LsePair {
+  float m, s;
+};
+__device__ __forceinline__ LsePair lse_merge(LsePair x, LsePair y) {
+  const float M = fmaxf(x.m, y.m);
+  return {M, x.s * __builtin_amdgcn_exp2f(x.m - M) + y.s * __builtin_amdgcn_exp2f(y.m - M)};
+}
+__device__ __forceinline__ LsePair lse_xor(LsePair p, int o) {
+  return lse_merge(p, {__shfl_xor(p.m, o), __shfl_xor(p.s, o)});
+}
+
+template <int NM, int NE, bool LS>
+struct LseAcc {
+  float m[NM][NE], s[NM][NE];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < NM; ++i)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        m[i][e] = kLseNone;
+        s[i][e] = 0.0f;
+      }
+  }
+  // fold logit l of a valid (row, batch) pair into entry (i, e)
+  __device__ __forceinline__ void add(int i, int e, float l, bool ok) {
+    const float y = l * kLog2e;
+    const float M = ok ? fmaxf(m[i][e], y) : m[i][e];
+    s[i][e] = s[i][e] * __builtin_amdgcn_exp2f(m[i][e] - M) + (ok ? __builtin_amdgcn_exp2f(y - M) : 0.0f);
+    m[i][e] = M;
+  }
+};
+template <int NM, int NE>
+struct LseAcc<NM, NE, false> {
+  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void add(int, int, float, bool) {}
+};
+
 // Fig. 7 epilogue for the result entries of one M block, then the local
 // selection (Fig. 8 step 1): logit = bf16(((acc_hi s_hi + acc_lo s_lo) s_w) +
 // base) for int8 W, bf16(acc + base) for bf16 W; score = logit (T=0) or
@@ -472,12 +518,14 @@ __device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Role
 // Branch-free: lanes without a valid (row, batch) pair contribute key 0.
 // With NZ, T=1 noise comes from LDS (computed one step ahead):
 // noise[b * a.noise_stride + (v - row0)], row0 = the workgroup's first row.
-template <int WT, int BB, int TEMP, bool NZ>
+// With LS, the logit also enters the running log-sum-exp pairs.
+template <int WT, int BB, int TEMP, bool NZ, bool LS>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                          const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
                                          float sw, const uint32_t (&bv)[Geo<WT, BB>::NE],
                                          const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                          typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                         LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
                                          const float* noise, int row0) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
@@ -499,6 +547,7 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
     if (a.logits != nullptr) {  // uniform: skipped entirely when logits are not requested
       if (okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
     }
+    ls.add(m, e, bf16_f32(lg), okb);
     typename LKey<TEMP>::T k;
     if (TEMP == 0) {
       k = (ord16(lg) << 16) | lrow;
@@ -560,13 +609,14 @@ __device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB
 
 // Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), one tile of
 // prefetch.  `cur` holds tile i0 of this step, loaded before the step began.
-template <int WT, int BB, int TEMP, int NWV, bool NZ>
+template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
                                              TileBuf<WT, BB> cur,
                                              const v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH],
                                              const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                              typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
+                                             LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
                                              const float* noise) {
   const int row0 = tb * kTileRows;
   using Gm = Geo<WT, BB>;
@@ -587,7 +637,7 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
         else acc = mma(Aop[m][0][c], cur.w[c], acc);
       }
       if (WT == 0) acc = acc + acc2;
-      epilogue<WT, BB, TEMP, NZ>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, noise, row0);
+      epilogue<WT, BB, TEMP, NZ, LS>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, ls, noise, row0);
     }
     if (i + 1 < nw) cur = nxt;
   }
@@ -623,6 +673,73 @@ __device__ __forceinline__ void reduce_to_lds(const Roles<WT, BB>& ro, int w,
   }
 }
 
+// Log-sum-exp pairs of one wave: merged inside each 16-lane row, then the
+// four rows per batch row (same mapping as the keys); lane 0 writes
+// lred[w][b] for b < BB.
+template <int WT, int BB, bool LS>
+__device__ __forceinline__ void lse_reduce_to_lds(const Roles<WT, BB>& ro, int w,
+                                                  const LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
+                                                  float2* lred) {
+  if constexpr (LS) {
+    using Gm = Geo<WT, BB>;
+    LsePair acc_b[BB];
+#pragma unroll
+    for (int b = 0; b < BB; ++b) acc_b[b] = {kLseNone, 0.0f};
+#pragma unroll
+    for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+      for (int e = 0; e < Gm::NE; ++e) {
+        LsePair p = {ls.m[m][e], ls.s[m][e]};
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) p = lse_xor(p, o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cw0 = (4 * q) % Gm::RPS;
+          const int b = WT == 0 ? (m * Gm::RPS + cw0) / 2 + e : m * Gm::RPS + cw0 + e;
+          if (b < BB)
+            acc_b[b] = lse_merge(acc_b[b], {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.m), 16 * q)),
+                                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.s), 16 * q))});
+        }
+      }
+    if (ro.lane == 0) {
+#pragma unroll
+      for (int b = 0; b < BB; ++b) lred[w * kMaxB + b] = make_float2(acc_b[b].m, acc_b[b].s);
+    }
+  }
+}
+
+// The workgroup's pair of each batch row (lanes b < B of one wave) to
+// lse_part[b][t][g] of a grid of G workgroups.
+__device__ __forceinline__ void lse_store_partial(const WalkArgs& a, const float2* lred, int nw, int t, int g,
+                                                  int G, int lane) {
+  if (lane < a.B) {
+    LsePair p = {kLseNone, 0.0f};
+    for (int ww = 0; ww < nw; ++ww) {
+      const float2 q = lred[ww * kMaxB + lane];
+      p = lse_merge(p, {q.x, q.y});
+    }
+    ((float2*)a.lse_part)[((size_t)lane * a.gamma + t) * G + g] = make_float2(p.m, p.s);
+  }
+}
+
+// Merge the partials of all G workgroups of every (row, step) into lse.
+// One wave per (row, step), nw waves.
+__device__ __forceinline__ void lse_finish(const WalkArgs& a, int G, int tid, int nw) {
+  const int w = tid >> 6, lane = tid & 63;
+  const int n = a.B * a.gamma;
+  for (int p = w; p < n; p += nw) {
+    LsePair acc = {kLseNone, 0.0f};
+    const float2* src = (const float2*)a.lse_part + (size_t)p * G;
+    for (int i = lane; i < G; i += 64) {
+      const float2 q = src[i];
+      acc = lse_merge(acc, {q.x, q.y});
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) acc = lse_xor(acc, o);
+    if (lane == 0) a.lse[p] = (acc.m + log2f(acc.s)) * kLn2f;
+  }
+}
+
 __device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
   atomicCAS(&ctrl->err, 0u, code);
 }
@@ -648,6 +765,7 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
     else if (i < n1 + n2) p2[i - n1] = 0ull;
     else p3[i - n1 - n2] = 0ull;
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0) ctrl->lse_done[q] = 0u;
 }
 
 // Cross-workgroup selection of one step (Fig. 8), one wave per workgroup.
@@ -938,8 +1056,9 @@ __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned 
   if (acc == 0x9E3779B9u) *lds_dummy = 1;  // keeps the loads; the byte is never read
 }
 
-// The whole walk in one cooperative launch: grid = one workgroup per CU.
-template <int WT, int BB, int HEAD, int TEMP>
+// The whole walk in one persistent launch: grid = one workgroup per CU.
+// LS: also the per-step log normaliser of the logits (lse output).
+template <int WT, int BB, int HEAD, int TEMP, bool LS>
 __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkArgs a) {
   constexpr int NW = waves_for(HEAD, WT);
   constexpr int NT = NW * 64;
@@ -964,6 +1083,10 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   const int par = a.parity;
   constexpr bool CAND = stage_candidates(HEAD, WT, BB);
   constexpr bool NOISE = TEMP && HEAD == kHeadMarkov;  // noise one step ahead in LDS
+  // fixed-latent probe (Fig. 13b): the state is never advanced after step 0
+  const bool fixed = a.fixed_latent != 0;
+  const bool stage = CAND && !fixed;  // staged candidate rows feed the next latent
+  float2* lred = (float2*)(lds + lse_lds_offset(HEAD, WT, BB));
   const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
   char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
 
@@ -1050,7 +1173,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   for (int t = 0; t < a.gamma; ++t) {
     stamp(t, 0);
     // state -> latent (Markov: embedding row of x_t; recurrent: h_{t+1})
-    if (HEAD == kHeadRecurrent) recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj);
+    if (HEAD == kHeadRecurrent && (t == 0 || !fixed)) recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj);
     // scales of the latent rows (int8), issued with the latent gather
     float shi[Gm::NM][Gm::NE];
 #pragma unroll
@@ -1060,7 +1183,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         const int b = ro.bent(m, e);
         shi[m][e] = 0.0f;
         if (WT == 0 && b < BB && b < a.B) {
-          if (CAND && t > 0)
+          if (stage && t > 0)
             shi[m][e] = ((const float*)(lds + kOffShs))[((const int*)(lds + kOffWin))[b]];
           else
             shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
@@ -1070,7 +1193,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     TileBuf<WT, BB> first;
     if (nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i Aop[Gm::NM][Gm::S][Gm::CH];
-    if (CAND && t > 0)
+    if (stage && t > 0)
       load_latent_staged<WT, BB>(a, ro, lds, Aop);
     else
       load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
@@ -1083,6 +1206,8 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
       for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0;
+    LseAcc<Gm::NM, Gm::NE, LS> ls;
+    ls.init();
 
     // projection over the register-resident tiles, S tiles per accumulator
 #pragma unroll
@@ -1107,23 +1232,27 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
             }
           }
           if (WT == 0) acc = acc + acc2;
-          epilogue<WT, BB, TEMP, NOISE>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0), gok[gi],
-                                 gsw[gi], bnx[gi][m], shi, best, noise, row0);
+          epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0),
+                                            gok[gi], gsw[gi], bnx[gi][m], shi, best, ls, noise, row0);
         }
       }
     }
     // LDS-resident and streamed tiles
     if (nreg < nw)
-      stream_tiles<WT, BB, TEMP, NW, NOISE>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, noise);
+      stream_tiles<WT, BB, TEMP, NW, NOISE, LS>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, ls,
+                                                noise);
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
     // for every workgroup -> common winner.
     reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
+    lse_reduce_to_lds<WT, BB, LS>(ro, w, ls, lred);
     __syncthreads();
     stamp(t, 2);
+    // the workgroup's log-sum-exp pairs of this step, by the last wave
+    if (LS && w == NW - 1) lse_store_partial(a, lred, NW, t, g, G, ro.lane);
     if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
-    if (CAND && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
+    if (stage && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
       make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
@@ -1149,19 +1278,36 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
           *sflag = 1;
           x = 0;
         }
-        sx[lane] = x;
+        if (!fixed) sx[lane] = x;
         if (g == 0) a.tokens[lane * a.gamma + t] = x;
       }
       stamp(t, 3);
     }
     // recurrent: A h_{t+1} for the next step while wave 0 waits
-    if (HEAD == kHeadRecurrent && t + 1 < a.gamma) recurrent_matvec<BB>(a, tid, lds, racc);
+    if (HEAD == kHeadRecurrent && t + 1 < a.gamma && !fixed) recurrent_matvec<BB>(a, tid, lds, racc);
     __syncthreads();
     if (*sflag) return;
   }
   if (HEAD == kHeadRecurrent && g == 0 && a.state) {
     const float* h = (const float*)(lds + kOffH);
     for (int i = tid; i < a.B * kR; i += NT) a.state[i] = h[i];
+  }
+  if constexpr (LS) {
+    // The last workgroup to get here merges every workgroup's partials: the
+    // wave that stored them releases them, one counter per walk orders the
+    // workgroups, and the last one acquires them all.
+    if (w == NW - 1) __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned done =
+          __hip_atomic_fetch_add(&ctrl->lse_done[par], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      *sflag = done == (unsigned)(G - 1) ? 2 : 0;
+    }
+    __syncthreads();
+    if (*sflag == 2) {
+      __threadfence();
+      lse_finish(a, G, tid, NW);
+    }
   }
 }
 
@@ -1171,10 +1317,11 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
 
 constexpr int kStepWaves = 4;
 
-template <int WT, int BB, int TEMP>
+template <int WT, int BB, int TEMP, bool LS>
 __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   using Gm = Geo<WT, BB>;
   __shared__ unsigned long long red[kWaves * kMaxB];
+  __shared__ float2 lred[LS ? kStepWaves * kMaxB : 1];
   __shared__ int sx[kMaxB];
   const int tid = threadIdx.x, w = tid >> 6;
   const Roles<WT, BB> ro(tid & 63);
@@ -1184,15 +1331,14 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   const int par = a.parity;
   if (t == 0) clear_next_walk(ctrl, par);
   if (tid < a.B) {
-    int x;
-    if (t == 0) {
-      x = a.x0[tid];
-    } else {
+    int x = a.x0[tid];
+    if (t > 0) {
       unsigned long long k = 0ull;
 #pragma unroll
       for (int i = 0; i < kSub; ++i) k = umax64(k, ld_agent(&ctrl->ss[par][t - 1][tid][i]));
-      x = key_token(k);
-      if (g == 0) a.tokens[tid * a.gamma + t - 1] = x;
+      const int xt = key_token(k);
+      if (g == 0) a.tokens[tid * a.gamma + t - 1] = xt;
+      if (!a.fixed_latent) x = xt;  // the fixed-latent probe keeps the latent of x0
     }
     if (x < 0 || x >= a.V) {
       latch_error(ctrl, 6u);
@@ -1220,14 +1366,18 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
     for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0;
+  LseAcc<Gm::NM, Gm::NE, LS> ls;
+  ls.init();
   if (nw > 0) {
     TileBuf<WT, BB> first;
     fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
-    stream_tiles<WT, BB, TEMP, kStepWaves, false>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best,
-                                           (const float*)nullptr);
+    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best,
+                                                      ls, (const float*)nullptr);
   }
   reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
+  lse_reduce_to_lds<WT, BB, LS>(ro, w, ls, lred);
   __syncthreads();
+  if (LS && w == 1) lse_store_partial(a, lred, kStepWaves, t, g, G, ro.lane);
   if (tid < a.B) {
     typename LKey<TEMP>::T lk = 0;
     for (int ww = 0; ww < kStepWaves; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + tid]);
@@ -1236,8 +1386,10 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   }
 }
 
-// Last token of a step-wise walk.
-__global__ void finish_kernel(WalkArgs a) {
+// Last token of a step-wise walk, and the log normalisers from the step
+// kernels' partials (grid G of the step kernels).
+constexpr int kFinishWaves = 4;
+__global__ __launch_bounds__(kFinishWaves * 64) void finish_kernel(WalkArgs a, int G) {
   const int b = threadIdx.x;
   if (b < a.B) {
     unsigned long long k = 0ull;
@@ -1245,6 +1397,7 @@ __global__ void finish_kernel(WalkArgs a) {
     const int x = key_token(k);
     a.tokens[b * a.gamma + a.gamma - 1] = (x >= 0 && x < a.V) ? x : 0;
   }
+  if (a.lse) lse_finish(a, G, threadIdx.x, kFinishWaves);
 }
 
 // ----------------------------------------------------------------------------
@@ -1281,33 +1434,34 @@ hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s) 
 // launch guarantees it but costs ~18 us more per launch on MI355X.  Either
 // way a workgroup that waits too long in the exchange latches WTS_ERR_TIMEOUT
 // and exits, so the grid always drains.
-template <int WT, int BB, int HEAD, int TEMP>
+template <int WT, int BB, int HEAD, int TEMP, bool LS>
 static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   void* args[] = {(void*)&a};
-  if (coop)
-    return hipLaunchCooperativeKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid),
-                                      dim3(waves_for(HEAD, WT) * 64),
-                                      args, (unsigned)lds_bytes, s);
-  return hipLaunchKernel((const void*)walk_kernel<WT, BB, HEAD, TEMP>, dim3(grid), dim3(waves_for(HEAD, WT) * 64), args,
-                         (size_t)lds_bytes, s);
+  const void* fn = (const void*)walk_kernel<WT, BB, HEAD, TEMP, LS>;
+  const dim3 blk(waves_for(HEAD, WT) * 64);
+  if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), blk, args, (unsigned)lds_bytes, s);
+  return hipLaunchKernel(fn, dim3(grid), blk, args, (size_t)lds_bytes, s);
 }
 
-template <int WT, int HEAD, int TEMP>
+template <int WT, int HEAD, int TEMP, bool LS>
 static hipError_t launch_walk_bb(int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   switch (BB) {
-    case 1: return launch_walk_t<WT, 1, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
-    case 2: return launch_walk_t<WT, 2, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
-    case 4: return launch_walk_t<WT, 4, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
-    case 8: return launch_walk_t<WT, 8, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
-    case 16: return launch_walk_t<WT, 16, HEAD, TEMP>(a, grid, lds_bytes, coop, s);
+    case 1: return launch_walk_t<WT, 1, HEAD, TEMP, LS>(a, grid, lds_bytes, coop, s);
+    case 2: return launch_walk_t<WT, 2, HEAD, TEMP, LS>(a, grid, lds_bytes, coop, s);
+    case 4: return launch_walk_t<WT, 4, HEAD, TEMP, LS>(a, grid, lds_bytes, coop, s);
+    case 8: return launch_walk_t<WT, 8, HEAD, TEMP, LS>(a, grid, lds_bytes, coop, s);
+    case 16: return launch_walk_t<WT, 16, HEAD, TEMP, LS>(a, grid, lds_bytes, coop, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int WT, int HEAD>
 static hipError_t launch_walk_temp(int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
-  return a.temperature ? launch_walk_bb<WT, HEAD, 1>(BB, a, grid, lds_bytes, coop, s)
-                       : launch_walk_bb<WT, HEAD, 0>(BB, a, grid, lds_bytes, coop, s);
+  if (a.lse)
+    return a.temperature ? launch_walk_bb<WT, HEAD, 1, true>(BB, a, grid, lds_bytes, coop, s)
+                         : launch_walk_bb<WT, HEAD, 0, true>(BB, a, grid, lds_bytes, coop, s);
+  return a.temperature ? launch_walk_bb<WT, HEAD, 1, false>(BB, a, grid, lds_bytes, coop, s)
+                       : launch_walk_bb<WT, HEAD, 0, false>(BB, a, grid, lds_bytes, coop, s);
 }
 
 hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
@@ -1318,36 +1472,42 @@ hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_b
                                : launch_walk_temp<1, kHeadRecurrent>(BB, a, grid, lds_bytes, coop, s);
 }
 
-template <int WT, int TEMP>
+template <int WT, int TEMP, bool LS>
 static hipError_t launch_step_t(int BB, const WalkArgs& a, int grid, hipStream_t s) {
   const dim3 blk(kStepWaves * 64);
   switch (BB) {
-    case 1: step_kernel<WT, 1, TEMP><<<grid, blk, 0, s>>>(a); break;
-    case 2: step_kernel<WT, 2, TEMP><<<grid, blk, 0, s>>>(a); break;
-    case 4: step_kernel<WT, 4, TEMP><<<grid, blk, 0, s>>>(a); break;
-    case 8: step_kernel<WT, 8, TEMP><<<grid, blk, 0, s>>>(a); break;
-    case 16: step_kernel<WT, 16, TEMP><<<grid, blk, 0, s>>>(a); break;
+    case 1: step_kernel<WT, 1, TEMP, LS><<<grid, blk, 0, s>>>(a); break;
+    case 2: step_kernel<WT, 2, TEMP, LS><<<grid, blk, 0, s>>>(a); break;
+    case 4: step_kernel<WT, 4, TEMP, LS><<<grid, blk, 0, s>>>(a); break;
+    case 8: step_kernel<WT, 8, TEMP, LS><<<grid, blk, 0, s>>>(a); break;
+    case 16: step_kernel<WT, 16, TEMP, LS><<<grid, blk, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s) {
-  if (wtype == 0) return a.temperature ? launch_step_t<0, 1>(BB, a, grid, s) : launch_step_t<0, 0>(BB, a, grid, s);
-  return a.temperature ? launch_step_t<1, 1>(BB, a, grid, s) : launch_step_t<1, 0>(BB, a, grid, s);
+template <int WT>
+static hipError_t launch_step_w(int BB, const WalkArgs& a, int grid, hipStream_t s) {
+  if (a.lse)
+    return a.temperature ? launch_step_t<WT, 1, true>(BB, a, grid, s) : launch_step_t<WT, 0, true>(BB, a, grid, s);
+  return a.temperature ? launch_step_t<WT, 1, false>(BB, a, grid, s) : launch_step_t<WT, 0, false>(BB, a, grid, s);
 }
 
-hipError_t launch_finish(const WalkArgs& a, hipStream_t s) {
-  finish_kernel<<<1, 64, 0, s>>>(a);
+hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s) {
+  return wtype == 0 ? launch_step_w<0>(BB, a, grid, s) : launch_step_w<1>(BB, a, grid, s);
+}
+
+hipError_t launch_finish(const WalkArgs& a, int grid, hipStream_t s) {
+  finish_kernel<<<1, kFinishWaves * 64, 0, s>>>(a, grid);
   return hipGetLastError();
 }
 
-template <int WT, int HEAD, int TEMP>
+template <int WT, int HEAD, int TEMP, bool LS>
 static hipError_t set_lds_attr(int lds_bytes) {
   hipError_t e = hipSuccess;
-  const void* fns[] = {(const void*)walk_kernel<WT, 1, HEAD, TEMP>, (const void*)walk_kernel<WT, 2, HEAD, TEMP>,
-                       (const void*)walk_kernel<WT, 4, HEAD, TEMP>, (const void*)walk_kernel<WT, 8, HEAD, TEMP>,
-                       (const void*)walk_kernel<WT, 16, HEAD, TEMP>};
+  const void* fns[] = {(const void*)walk_kernel<WT, 1, HEAD, TEMP, LS>, (const void*)walk_kernel<WT, 2, HEAD, TEMP, LS>,
+                       (const void*)walk_kernel<WT, 4, HEAD, TEMP, LS>, (const void*)walk_kernel<WT, 8, HEAD, TEMP, LS>,
+                       (const void*)walk_kernel<WT, 16, HEAD, TEMP, LS>};
   for (const void* f : fns) {
     const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (r != hipSuccess) e = r;
@@ -1355,15 +1515,21 @@ static hipError_t set_lds_attr(int lds_bytes) {
   return e;
 }
 
-hipError_t prepare_kernels(int lds_bytes) {
+template <bool LS>
+static hipError_t set_lds_attr_all(int lds_bytes) {
   const hipError_t r[] = {
-      set_lds_attr<0, kHeadMarkov, 0>(lds_bytes), set_lds_attr<0, kHeadMarkov, 1>(lds_bytes),
-      set_lds_attr<0, kHeadRecurrent, 0>(lds_bytes), set_lds_attr<0, kHeadRecurrent, 1>(lds_bytes),
-      set_lds_attr<1, kHeadMarkov, 0>(lds_bytes), set_lds_attr<1, kHeadMarkov, 1>(lds_bytes),
-      set_lds_attr<1, kHeadRecurrent, 0>(lds_bytes), set_lds_attr<1, kHeadRecurrent, 1>(lds_bytes)};
+      set_lds_attr<0, kHeadMarkov, 0, LS>(lds_bytes), set_lds_attr<0, kHeadMarkov, 1, LS>(lds_bytes),
+      set_lds_attr<0, kHeadRecurrent, 0, LS>(lds_bytes), set_lds_attr<0, kHeadRecurrent, 1, LS>(lds_bytes),
+      set_lds_attr<1, kHeadMarkov, 0, LS>(lds_bytes), set_lds_attr<1, kHeadMarkov, 1, LS>(lds_bytes),
+      set_lds_attr<1, kHeadRecurrent, 0, LS>(lds_bytes), set_lds_attr<1, kHeadRecurrent, 1, LS>(lds_bytes)};
   for (hipError_t e : r)
     if (e != hipSuccess) return e;
   return hipSuccess;
+}
+
+hipError_t prepare_kernels(int lds_bytes) {
+  const hipError_t e = set_lds_attr_all<false>(lds_bytes);
+  return e != hipSuccess ? e : set_lds_attr_all<true>(lds_bytes);
 }
 
 }  // namespace wts

@@ -30,6 +30,7 @@ struct wts_ctx {
   const uint16_t* A = nullptr;
   const float* c = nullptr;
   Ctrl* ctrl = nullptr;
+  float* lse_part = nullptr;  // (max, sum) pairs of every workgroup, per row and step
   unsigned long long walks = 0;
   long long timeout_ticks = 0;
 };
@@ -54,6 +55,9 @@ int batch_bucket(int B) {
 }
 
 int tile_bytes(int wtype) { return wtype == WTS_W_INT8 ? kTileBytesI8 : kTileBytesBF; }
+
+// Workgroups of one step-wise launch (8 tiles each).
+int step_grid(const wts_ctx* ctx) { return std::max(1, (ctx->tiles + 7) / 8); }
 
 
 // Gumbel noise of a T=1 persistent Markov walk is computed one step ahead
@@ -122,6 +126,7 @@ void free_ctx(wts_ctx* ctx) {
   (void)hipFree(ctx->Es);
   (void)hipFree(ctx->Eb);
   (void)hipFree(ctx->ctrl);
+  (void)hipFree(ctx->lse_part);
   delete ctx;
 }
 
@@ -197,6 +202,10 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   }
   if (st == WTS_OK && p->head == WTS_HEAD_MARKOV && p->wtype == WTS_W_BF16)
     st = dmalloc(&ctx->Eb, (size_t)p->V * kR * 2);
+  if (st == WTS_OK) {
+    const size_t groups = (size_t)std::max(ctx->grid, step_grid(ctx));
+    st = dmalloc(&ctx->lse_part, (size_t)p->max_batch * p->max_steps * groups * 2 * sizeof(float));
+  }
   if (st != WTS_OK) {
     free_ctx(ctx);
     return st;
@@ -233,13 +242,13 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   if (!ctx || !p) return WTS_ERR_INVALID_ARG;
   if (p->B < 1 || p->B > ctx->max_batch || p->gamma < 1 || p->gamma > ctx->max_steps) return WTS_ERR_INVALID_ARG;
   if (p->temperature != 0 && p->temperature != 1) return WTS_ERR_INVALID_ARG;
-  if (p->step_offset < 0 || p->reserved != 0) return WTS_ERR_INVALID_ARG;
+  if (p->step_offset < 0 || (p->flags & ~WTS_WALK_FIXED_LATENT) != 0) return WTS_ERR_INVALID_ARG;
   if (p->exec < WTS_EXEC_RESIDENT || p->exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
   if (!p->base || !p->x0 || !p->tokens_out) return WTS_ERR_INVALID_ARG;
   if (ctx->head == WTS_HEAD_RECURRENT && !p->h0) return WTS_ERR_INVALID_ARG;
   if (((uintptr_t)p->base & 1) || ((uintptr_t)p->x0 & 3) || ((uintptr_t)p->tokens_out & 3) ||
       ((uintptr_t)p->logits_out & 1) || ((uintptr_t)p->h0 & 3) || ((uintptr_t)p->state_out & 3) ||
-      ((uintptr_t)p->trace_out & 7))
+      ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
   DeviceGuard guard(ctx->device);
@@ -281,17 +290,20 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.state = p->state_out;
   a.trace = (long long*)p->trace_out;
   a.timeout_ticks = ctx->timeout_ticks;
+  a.fixed_latent = (p->flags & WTS_WALK_FIXED_LATENT) != 0;
+  a.lse = p->lse_out;
+  a.lse_part = ctx->lse_part;
   hipStream_t s = (hipStream_t)p->stream;
 
   hipError_t e;
   if (p->exec == WTS_EXEC_STEPWISE) {
-    const int grid = std::max(1, (ctx->tiles + 7) / 8);
+    const int grid = step_grid(ctx);
     e = hipSuccess;
     for (int t = 0; t < p->gamma && e == hipSuccess; ++t) {
       a.step = t;
       e = launch_step(ctx->wtype, BB, a, grid, s);
     }
-    if (e == hipSuccess) e = launch_finish(a, s);
+    if (e == hipSuccess) e = launch_finish(a, grid, s);
   } else {
     e = launch_walk(ctx->wtype, BB, a, ctx->grid, lds_bytes, ctx->cooperative, s);
   }

@@ -32,14 +32,14 @@ def make_head(d, t=None, **kw):
 
 
 def run(head, t, *, base=None, x0=None, h0=None, temperature=0, seed=0, step_offset=0, exec="resident",
-        logits=True, state=None):
+        logits=True, state=None, lse=False, fixed_latent=False):
     import torch
     base = t["base"] if base is None else base
     x0 = t["x0"] if x0 is None else x0
     h0 = t["h0"] if h0 is None else h0
     state = (head.head == "recurrent") if state is None else state
     o = head.walk(base, x0, h0=h0, temperature=temperature, seed=seed, step_offset=step_offset,
-                  logits=logits, state=state, exec=exec)
+                  logits=logits, state=state, exec=exec, lse=lse, fixed_latent=fixed_latent)
     torch.cuda.synchronize()
     err = head.error()
     assert err == "WTS_OK", err
@@ -48,15 +48,40 @@ def run(head, t, *, base=None, x0=None, h0=None, temperature=0, seed=0, step_off
         res["logits"] = o["logits"].view(torch.int16).cpu().numpy().view(np.uint16)
     if state:
         res["state"] = o["state"].cpu().numpy()
+    if lse:
+        res["lse"] = o["lse"].cpu().numpy()
     return res
 
 
-def oracle_walk(d, temperature=0, seed=0, step_offset=0, keep_z=False, base=None, x0=None, h0=None):
+def oracle_walk(d, temperature=0, seed=0, step_offset=0, keep_z=False, base=None, x0=None, h0=None,
+                keep_lse=False, fixed_latent=False):
     import oracle
     return oracle.walk(d["W"], d["E"], d["base"] if base is None else base,
                        d["x0"] if x0 is None else x0, wtype=d["wtype"], s_w=d["s_w"], head=d["head"],
                        A=d["A"], c=d["c"], h0=d["h0"] if h0 is None else h0,
-                       temperature=temperature, seed=seed, step_offset=step_offset, keep_z=keep_z)
+                       temperature=temperature, seed=seed, step_offset=step_offset, keep_z=keep_z,
+                       keep_lse=keep_lse, fixed_latent=fixed_latent)
+
+
+# Log normaliser of the kernel: fp32 terms 2^(l log2 e - m) with one rounding
+# each (plus the v_exp_f32 error of about 1 ulp), summed in fp32 over at most
+# ~40 levels (per-lane running sums, 6 lane levels, waves, workgroups), then
+# (m + log2 s) ln 2 in fp32.  Relative error of the sum <= ~60 * 2^-24 ~ 4e-6,
+# i.e. an absolute error of about 4e-6 in lse, plus the final rounding of a
+# value below 64 (< 4e-6).  The bar is 1e-5 * max(1, |lse|) (the values here
+# are 5..40, so 5e-5..4e-4).
+LSE_RTOL = 1e-5
+
+
+def assert_lse_close(got_lse, logits_bits, what=""):
+    """lse of every (b, t) against the float64 normaliser of the same logits."""
+    from oracle.walk import log_normaliser
+    B, gamma = got_lse.shape
+    for b in range(B):
+        for t in range(gamma):
+            want = log_normaliser(logits_bits[b, t])
+            err = abs(float(got_lse[b, t]) - want)
+            assert err <= LSE_RTOL * max(1.0, abs(want)), f"{what}: lse b={b} t={t} gpu {got_lse[b, t]} want {want}"
 
 
 def assert_exact(got, ref, what=""):

@@ -31,8 +31,10 @@ def _brute_quant(u):
     return hi, lo, s_hi, s_hi / 256
 
 
-def _brute_walk(d, temperature=0, seed=0, step_offset=0):
-    """Every operation of the int8 Markov / recurrent walk with exact rationals."""
+def _brute_walk(d, temperature=0, seed=0, step_offset=0, fixed=False):
+    """Every operation of the int8 Markov / recurrent walk with exact rationals.
+
+    fixed: the fixed-latent probe (Fig. 13b) -- the state of step 0 is kept."""
     W, s_w, E, base, x0 = d["W"], d["s_w"], d["E"], d["base"], d["x0"]
     B, gamma, V = base.shape
     r = W.shape[1]
@@ -44,6 +46,8 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0):
         for t in range(gamma):
             if d["head"] == "markov":
                 lat = E[x]
+            elif fixed and t > 0:
+                lat = np.array(h, np.float32)
             else:
                 A = bf16_to_f32(d["A"])
                 hn = []
@@ -71,8 +75,9 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0):
                     g = oracle.gumbel_noise(seed, b, step_offset + t, np.array([v]))[0]
                     lg = rnd32(lg + _F(g))
                 scores.append((-lg, v))
-            x = min(scores)[1]
-            toks[b, t] = x
+            toks[b, t] = min(scores)[1]
+            if not fixed:
+                x = int(toks[b, t])
     return toks, logits
 
 
@@ -245,3 +250,89 @@ def test_bf16_walk_bruteforce_small():
             sc.append((-rnd_bf16(z), v))
         x = min(sc)[1]
         assert o["tokens"][0, t] == x
+
+
+@pytest.mark.parametrize("temperature", [0, 1])
+@pytest.mark.parametrize("head", ["markov", "recurrent"])
+def test_fixed_latent_brute_force(temperature, head):
+    # the probe of Fig. 13b on the toy shape: every op with exact rationals
+    r = 4 if head == "markov" else 16
+    d = datagen.make_inputs(12, r, 2, 4, head=head, seed=21)
+    toks, lg = _brute_walk(d, temperature, seed=4, fixed=True)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head=head, A=d["A"],
+                    c=d["c"], h0=d["h0"], temperature=temperature, seed=4, fixed_latent=True)
+    assert np.array_equal(o["tokens"], toks)
+    assert np.array_equal(o["logits"], lg)
+
+
+def test_fixed_latent_cyclic_successor():
+    # the cyclic-successor head walks x0+1, x0+2, ...; with the latent fixed at
+    # E[x0] every step picks x0+1
+    V, r = 12, 4
+    th = 2 * np.pi * np.arange(V) / V
+    d = datagen.make_inputs(V, r, 3, 5, seed=22)
+    d["W"] = np.zeros((V, r), np.int8)
+    d["W"][:, 0] = np.rint(127 * np.cos(th))
+    d["W"][:, 1] = np.rint(127 * np.sin(th))
+    d["s_w"] = np.full(V, 1 / 127, np.float32)
+    d["E"] = np.zeros((V, r), np.float32)
+    d["E"][:, 0] = np.cos(np.roll(th, -1))
+    d["E"][:, 1] = np.sin(np.roll(th, -1))
+    d["base"][:] = 0
+    d["x0"] = np.array([3, 11, 6], np.int32)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], fixed_latent=True)
+    assert np.array_equal(o["tokens"], np.repeat(((d["x0"] + 1) % V)[:, None], 5, axis=1))
+
+
+@pytest.mark.parametrize("head", ["markov", "recurrent"])
+def test_fixed_latent_steps_are_one_step_walks(head):
+    # step t of the probe is the first step of a walk from x0 that reads base row t
+    d = datagen.make_inputs(300, 32, 2, 5, head=head, seed=23)
+    kw = dict(s_w=d["s_w"], head=head, A=d["A"], c=d["c"], h0=d["h0"])
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], fixed_latent=True, **kw)
+    for t in range(5):
+        one = oracle.walk(d["W"], d["E"], d["base"][:, t:t + 1], d["x0"], **kw)
+        assert np.array_equal(o["tokens"][:, t], one["tokens"][:, 0])
+        assert np.array_equal(o["logits"][:, t], one["logits"][:, 0])
+
+
+def test_log_normaliser_closed_forms():
+    from oracle.walk import log_normaliser
+    import math
+    # equal logits: ln(V e^c) = c + ln V
+    for c, V in [(1.5, 1000), (-7.25, 1), (12.0, 151936)]:
+        lg = np.full(V, bf16_rne(np.float32(c)), np.uint16)
+        assert abs(log_normaliser(lg) - (c + math.log(V))) < 1e-12 * max(1.0, abs(c))
+    # two values: k copies of a, n - k of b
+    a, b, k, n = 3.0, -2.5, 7, 5000
+    lg = np.full(n, bf16_rne(np.float32(b)), np.uint16)
+    lg[:k] = bf16_rne(np.float32(a))
+    want = a + math.log(k + (n - k) * math.exp(b - a))
+    assert abs(log_normaliser(lg) - want) < 1e-12
+    # exact shift invariance for bf16-exact shifts
+    rng = np.random.default_rng(24)
+    q = rng.integers(-64, 64, 3000).astype(np.float32) / 8
+    assert abs(log_normaliser(bf16_rne(q + 4)) - log_normaliser(bf16_rne(q)) - 4) < 1e-12
+
+
+def test_log_normaliser_matches_library():
+    from oracle.walk import log_normaliser
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(25)
+    lg = bf16_rne(rng.normal(0, 2, 20000).astype(np.float32))
+    l64 = bf16_to_f32(lg).astype(np.float64)
+    lse = log_normaliser(lg)
+    assert abs(lse - logsumexp(l64)) < 1e-11
+    # q = exp(l - lse) is the softmax of the logits and sums to one
+    assert np.allclose(np.exp(l64 - lse), softmax(l64), rtol=1e-12, atol=0)
+    assert abs(np.exp(l64 - lse).sum() - 1.0) < 1e-12
+
+
+def test_walk_lse_is_normaliser_of_its_logits():
+    d = datagen.make_inputs(700, 32, 2, 4, seed=26)
+    o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], temperature=1, seed=2,
+                    keep_lse=True)
+    from oracle.walk import log_normaliser
+    for b in range(2):
+        for t in range(4):
+            assert o["lse"][b, t] == log_normaliser(o["logits"][b, t])
