@@ -262,6 +262,32 @@ def main():
         for ex in ("stream", "stepwise"):
             extras[f"fit_{ex}"] = fit_steps(head, d, t, exec=ex)
             log(ex, extras[f"fit_{ex}"])
+        # Fig. 13b analog: the fixed-latent probe repeats projection and selection
+        # with the latent of step 0; the difference of the slopes is the state advance
+        fx = fit_steps(head, d, t, fixed_latent=True)
+        extras["fit_fixed_latent"] = fx
+        extras["advance_us_per_step"] = round(fit["per_step_us"] - fx["per_step_us"], 3)
+        extras["breakdown_fixed_latent"] = breakdown(head, t, fixed_latent=True)
+        log("fixed latent", fx, extras["breakdown_fixed_latent"])
+        # verification-ready output: cost of the per-step log normaliser at T=1
+        _, u0 = timed_walks(head, t, 100, 10, temperature=1, seed=0)
+        _, u1 = timed_walks(head, t, 100, 10, temperature=1, seed=0, lse=True)
+        extras["lse_t1"] = {"median_us_without": round(float(np.median(u0)), 2),
+                            "median_us_with": round(float(np.median(u1)), 2)}
+        log("lse", extras["lse_t1"])
+        # Fig. 12 analog: placement of the shard between registers and LDS
+        # (B=1, greedy); register tiles per wave r, the rest of the shard in LDS
+        place = []
+        for r in range(0, plan["reg_tiles"] + 1):
+            hp, _ = make_head(d, t, resident_tiles=r)
+            pp = hp.plan(1)
+            fp = fit_steps(hp, d, t, n=50, warmup=5)
+            place.append({"reg_tiles": pp["reg_tiles"], "lds_tiles": pp["lds_tiles"],
+                          "stream_tiles": pp["stream_tiles"], "per_step_us": round(fp["per_step_us"], 3),
+                          "entry_us": round(fp["entry_us"], 2)})
+            hp.close()
+            log("placement", place[-1])
+        extras["placement_int8_v151936_b1"] = place
         # batch / temperature sweep on the same W (partial residency above B=4 is not needed here:
         # the shard stays fully on chip, registers then LDS)
         sweep = []
@@ -296,6 +322,20 @@ def main():
         h3.close()
         del t3, d3
         torch.cuda.empty_cache()
+        # other residency points: bf16 W at V=151,936 and int8 W at V=248,320, both on chip
+        for name, V_, wt in (("markov_bf16_v151936", 151936, "bf16"), ("markov_int8_v248320", 248320, "int8")):
+            dx = datagen.make_inputs(V_, 256, 1, 16, wtype=wt, seed=0)
+            hx, tx = make_head(dx)
+            px = hx.plan(1)
+            fx = fit_steps(hx, dx, tx, n=50, warmup=5)
+            extras[name] = {"per_step_us": round(fx["per_step_us"], 3), "entry_us": round(fx["entry_us"], 2),
+                            "median_us_g16": round(fx["median_us"][-1], 2),
+                            "resident_MB": round(px["resident_bytes"] / 1e6, 1),
+                            "streamed_MB_per_step": round(px["streamed_bytes"] / 1e6, 1)}
+            log(name, extras[name])
+            hx.close()
+            del tx, dx
+            torch.cuda.empty_cache()
         # recurrent head, 15 steps
         d4 = datagen.config_inputs(4)
         h4, t4 = make_head(d4)

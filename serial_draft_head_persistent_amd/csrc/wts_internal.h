@@ -44,10 +44,12 @@ constexpr bool stage_candidates(int head, int wtype, int BB) {
 }
 // LDS bytes in front of the LDS-resident W tiles.
 constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
-  return head == kHeadRecurrent ? 32768 + kR * kR * 2 : stage_candidates(head, wtype, BB) ? 20480 : 3072;
+  return head == kHeadRecurrent ? 32768 + kR * kR * 2 : stage_candidates(head, wtype, BB) ? 21504 : 5120;
 }
-// LDS offset of the per-wave log-sum-exp pairs (float2 [kWaves][kMaxB]), in
-// a part of the scratch that nothing else of that kernel uses.
+// LDS offset of the log-sum-exp pairs: per wave and batch row (float2
+// [kWaves][kMaxB], 1 KiB), then the exchange wave's raw pairs (float2
+// [result entries][64], at most 2 KiB; 1 KiB at B=1), in a part of the
+// scratch that nothing else of that kernel uses.
 constexpr int lse_lds_offset(int head, int wtype, int BB) {
   return head == kHeadRecurrent ? 26624 : stage_candidates(head, wtype, BB) ? 18688 : 2048;
 }
@@ -68,8 +70,7 @@ struct Ctrl {
   // step-wise walk: device-scope max per (step, batch row, sub-slot)
   unsigned long long ss[2][kMaxSteps][kMaxB][kSub];
   unsigned int err;                               // latched wts_status
-  unsigned int lse_done[2];                       // per walk parity: workgroups done with their partials
-  unsigned int pad[61];
+  unsigned int pad[63];
 };
 
 struct WalkArgs {
@@ -121,7 +122,8 @@ hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s);
 hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_bytes,
                        bool cooperative, hipStream_t s);
 hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s);
-hipError_t launch_finish(const WalkArgs& a, int grid, hipStream_t s);
+hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
+hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);
 
 }  // namespace wts

@@ -289,6 +289,7 @@ constexpr int kOffShi = kOffX + 4 * kMaxB;        // float [kMaxB]
 constexpr int kOffFlag = kOffShi + 4 * kMaxB;     // int
 constexpr int kOffDone = kOffFlag + 8;           // int: step + 1 whose exchange finished
 constexpr int kOffWin = kOffDone + 8;            // int [kMaxB]: staged row holding the winner
+constexpr int kOffLseCnt = 1240;                 // int: waves done with this step's log-sum-exp pairs
 constexpr int kOffZero = 1280;                   // 256 zero bytes (A-operand source of other slots)
 constexpr int kOffCand = 1536;                   // u64 [kGroups][2]: group maxima seen so far
 constexpr int kOffRows = 2048;                   // [kGroups * 2][512]: staged candidate rows (hi | lo)
@@ -484,6 +485,16 @@ __device__ __forceinline__ LsePair lse_merge(LsePair x, LsePair y) {
 __device__ __forceinline__ LsePair lse_xor(LsePair p, int o) {
   return lse_merge(p, {__shfl_xor(p.m, o), __shfl_xor(p.s, o)});
 }
+// Merge over the 16 lanes of each DPP row (the butterfly of row_max).
+#define WTS_DPPF(x, c) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (c), 0xF, 0xF, false))
+__device__ __forceinline__ LsePair lse_row_merge(LsePair p) {
+  p = lse_merge(p, {WTS_DPPF(p.m, 0xB1), WTS_DPPF(p.s, 0xB1)});
+  p = lse_merge(p, {WTS_DPPF(p.m, 0x4E), WTS_DPPF(p.s, 0x4E)});
+  p = lse_merge(p, {WTS_DPPF(p.m, 0x141), WTS_DPPF(p.s, 0x141)});
+  p = lse_merge(p, {WTS_DPPF(p.m, 0x140), WTS_DPPF(p.s, 0x140)});
+  return p;
+}
+#undef WTS_DPPF
 
 template <int NM, int NE, bool LS>
 struct LseAcc {
@@ -673,8 +684,19 @@ __device__ __forceinline__ void reduce_to_lds(const Roles<WT, BB>& ro, int w,
   }
 }
 
-// Log-sum-exp pairs of one wave: merged inside each 16-lane row, then the
-// four rows per batch row (same mapping as the keys); lane 0 writes
+// Whether result entry e of M block m holds a batch row of the bucket for
+// some lane (the four 16-lane rows map to batch rows as in reduce_to_lds).
+template <int WT, int BB>
+__device__ constexpr bool entry_used(int m, int e) {
+  using Gm = Geo<WT, BB>;
+  bool used = false;
+  for (int q = 0; q < 4; ++q)
+    used = used || (WT == 0 ? (m * Gm::RPS + (4 * q) % Gm::RPS) / 2 + e : m * Gm::RPS + (4 * q) % Gm::RPS + e) < BB;
+  return used;
+}
+
+// Log-sum-exp pairs of one wave: merged inside each 16-lane row (DPP), then
+// the four rows per batch row (same mapping as the keys); lane 0 writes
 // lred[w][b] for b < BB.
 template <int WT, int BB, bool LS>
 __device__ __forceinline__ void lse_reduce_to_lds(const Roles<WT, BB>& ro, int w,
@@ -689,9 +711,8 @@ __device__ __forceinline__ void lse_reduce_to_lds(const Roles<WT, BB>& ro, int w
     for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
       for (int e = 0; e < Gm::NE; ++e) {
-        LsePair p = {ls.m[m][e], ls.s[m][e]};
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) p = lse_xor(p, o);
+        if (!entry_used<WT, BB>(m, e)) continue;  // compile-time: entry unused by this batch bucket
+        const LsePair p = lse_row_merge({ls.m[m][e], ls.s[m][e]});
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int cw0 = (4 * q) % Gm::RPS;
@@ -722,22 +743,72 @@ __device__ __forceinline__ void lse_store_partial(const WalkArgs& a, const float
   }
 }
 
-// Merge the partials of all G workgroups of every (row, step) into lse.
-// One wave per (row, step), nw waves.
-__device__ __forceinline__ void lse_finish(const WalkArgs& a, int G, int tid, int nw) {
-  const int w = tid >> 6, lane = tid & 63;
-  const int n = a.B * a.gamma;
-  for (int p = w; p < n; p += nw) {
-    LsePair acc = {kLseNone, 0.0f};
-    const float2* src = (const float2*)a.lse_part + (size_t)p * G;
-    for (int i = lane; i < G; i += 64) {
-      const float2 q = src[i];
-      acc = lse_merge(acc, {q.x, q.y});
-    }
+// The exchange wave's raw pairs, handed to another wave through LDS
+// (lraw[entry][lane]) so that the exchange does not wait for their merge.
+template <int WT, int BB, bool LS>
+__device__ __forceinline__ void lse_stash(const Roles<WT, BB>& ro,
+                                          const LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls, float2* lraw) {
+  if constexpr (LS) {
+    using Gm = Geo<WT, BB>;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) acc = lse_xor(acc, o);
-    if (lane == 0) a.lse[p] = (acc.m + log2f(acc.s)) * kLn2f;
+    for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+      for (int e = 0; e < Gm::NE; ++e)
+        if (entry_used<WT, BB>(m, e)) lraw[(m * Gm::NE + e) * 64 + ro.lane] = make_float2(ls.m[m][e], ls.s[m][e]);
   }
+}
+
+// Per-step pairs of the workgroup while wave 0 runs the exchange: waves
+// 1..NW-1 merge their own pairs (the last of them also wave 0's stashed
+// pairs); the last wave to finish, found with an LDS counter, merges the
+// waves' pairs and stores the workgroup's pair of every batch row.
+template <int WT, int BB, int NW, bool LS>
+__device__ __forceinline__ void lse_workgroup(const WalkArgs& a, const Roles<WT, BB>& ro, int w,
+                                              const LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
+                                              float2* lred, const float2* lraw, int* cnt, int t, int g, int G) {
+  if constexpr (LS) {
+    using Gm = Geo<WT, BB>;
+    lse_reduce_to_lds<WT, BB, LS>(ro, w, ls, lred);
+    if (w == NW - 1) {
+      LseAcc<Gm::NM, Gm::NE, LS> l0;
+      l0.init();
+#pragma unroll
+      for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+        for (int e = 0; e < Gm::NE; ++e)
+          if (entry_used<WT, BB>(m, e)) {
+            const float2 q = lraw[(m * Gm::NE + e) * 64 + ro.lane];
+            l0.m[m][e] = q.x;
+            l0.s[m][e] = q.y;
+          }
+      lse_reduce_to_lds<WT, BB, LS>(ro, 0, l0, lred);
+    }
+    int last = 0;
+    if (ro.lane == 0)
+      last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == NW - 2;
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      lse_store_partial(a, lred, NW, t, g, G, ro.lane);
+      if (ro.lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+}
+
+// Merge the partials of all G workgroups of every (row, step) into lse:
+// one wave per (row, step), launched after the walk on the same stream.
+constexpr int kLseWaves = 4;
+__global__ __launch_bounds__(kLseWaves * 64) void lse_kernel(WalkArgs a, int G) {
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * kLseWaves + (threadIdx.x >> 6);
+  if (p >= a.B * a.gamma) return;
+  LsePair acc = {kLseNone, 0.0f};
+  const float2* src = (const float2*)a.lse_part + (size_t)p * G;
+  for (int i = lane; i < G; i += 64) {
+    const float2 q = src[i];
+    acc = lse_merge(acc, {q.x, q.y});
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) acc = lse_xor(acc, o);
+  if (lane == 0) a.lse[p] = (acc.m + log2f(acc.s)) * kLn2f;
 }
 
 __device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
@@ -765,7 +836,6 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
     else if (i < n1 + n2) p2[i - n1] = 0ull;
     else p3[i - n1 - n2] = 0ull;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) ctrl->lse_done[q] = 0u;
 }
 
 // Cross-workgroup selection of one step (Fig. 8), one wave per workgroup.
@@ -1085,8 +1155,10 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   constexpr bool NOISE = TEMP && HEAD == kHeadMarkov;  // noise one step ahead in LDS
   // fixed-latent probe (Fig. 13b): the state is never advanced after step 0
   const bool fixed = a.fixed_latent != 0;
-  const bool stage = CAND && !fixed;  // staged candidate rows feed the next latent
-  float2* lred = (float2*)(lds + lse_lds_offset(HEAD, WT, BB));
+  const bool stage = CAND && !fixed;  // stage the exchange's candidate rows for the next latent
+  float2* lred = (float2*)(lds + lse_lds_offset(HEAD, WT, BB));  // [kWaves][kMaxB]
+  float2* lraw = lred + kWaves * kMaxB;                           // [entries][64]
+  int* lcnt = (int*)(lds + kOffLseCnt);
   const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
   char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
 
@@ -1120,7 +1192,10 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   float* noise_lds = NOISE ? (float*)(lds + a.noise_off) : nullptr;
   const float* noise = noise_lds;
 
-  if (tid == 0) *sflag = 0;
+  if (tid == 0) {
+    *sflag = 0;
+    *lcnt = 0;
+  }
   if (CAND) {
     for (int i = tid; i < 64; i += NT) ((int*)(lds + kOffZero))[i] = 0;
     for (int i = tid; i < kGroups * 2; i += NT) ((unsigned long long*)(lds + kOffCand))[i] = 0ull;
@@ -1153,6 +1228,14 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   __syncthreads();
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
+  if (CAND && fixed) {
+    // the probe's latent, staged once where later steps read staged rows
+    if (tid < kRowBytes / 16) ((int4*)(lds + kOffRows))[tid] = ((const int4*)(a.Eq + (size_t)sx[0] * 512))[tid];
+    if (tid == 0) {
+      ((float*)(lds + kOffShs))[0] = a.Es[sx[0]];
+      ((int*)(lds + kOffWin))[0] = 0;
+    }
+  }
 
   // Base logits of the register-resident groups and the first non-register
   // tile are loaded one step ahead, so their memory latency overlaps the
@@ -1183,7 +1266,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         const int b = ro.bent(m, e);
         shi[m][e] = 0.0f;
         if (WT == 0 && b < BB && b < a.B) {
-          if (stage && t > 0)
+          if (CAND && t > 0)
             shi[m][e] = ((const float*)(lds + kOffShs))[((const int*)(lds + kOffWin))[b]];
           else
             shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
@@ -1193,7 +1276,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     TileBuf<WT, BB> first;
     if (nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i Aop[Gm::NM][Gm::S][Gm::CH];
-    if (stage && t > 0)
+    if (CAND && t > 0)
       load_latent_staged<WT, BB>(a, ro, lds, Aop);
     else
       load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
@@ -1246,11 +1329,11 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
     // for every workgroup -> common winner.
     reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
-    lse_reduce_to_lds<WT, BB, LS>(ro, w, ls, lred);
+    if (w == 0) lse_stash<WT, BB, LS>(ro, ls, lraw);
     __syncthreads();
     stamp(t, 2);
-    // the workgroup's log-sum-exp pairs of this step, by the last wave
-    if (LS && w == NW - 1) lse_store_partial(a, lred, NW, t, g, G, ro.lane);
+    // the workgroup's log-sum-exp pairs of this step, merged during the exchange
+    if (w > 0) lse_workgroup<WT, BB, NW, LS>(a, ro, w, ls, lred, lraw, lcnt, t, g, G);
     if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
     if (stage && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
@@ -1291,23 +1374,6 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   if (HEAD == kHeadRecurrent && g == 0 && a.state) {
     const float* h = (const float*)(lds + kOffH);
     for (int i = tid; i < a.B * kR; i += NT) a.state[i] = h[i];
-  }
-  if constexpr (LS) {
-    // The last workgroup to get here merges every workgroup's partials: the
-    // wave that stored them releases them, one counter per walk orders the
-    // workgroups, and the last one acquires them all.
-    if (w == NW - 1) __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned done =
-          __hip_atomic_fetch_add(&ctrl->lse_done[par], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      *sflag = done == (unsigned)(G - 1) ? 2 : 0;
-    }
-    __syncthreads();
-    if (*sflag == 2) {
-      __threadfence();
-      lse_finish(a, G, tid, NW);
-    }
   }
 }
 
@@ -1386,10 +1452,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   }
 }
 
-// Last token of a step-wise walk, and the log normalisers from the step
-// kernels' partials (grid G of the step kernels).
-constexpr int kFinishWaves = 4;
-__global__ __launch_bounds__(kFinishWaves * 64) void finish_kernel(WalkArgs a, int G) {
+// Last token of a step-wise walk.
+__global__ void finish_kernel(WalkArgs a) {
   const int b = threadIdx.x;
   if (b < a.B) {
     unsigned long long k = 0ull;
@@ -1397,7 +1461,6 @@ __global__ __launch_bounds__(kFinishWaves * 64) void finish_kernel(WalkArgs a, i
     const int x = key_token(k);
     a.tokens[b * a.gamma + a.gamma - 1] = (x >= 0 && x < a.V) ? x : 0;
   }
-  if (a.lse) lse_finish(a, G, threadIdx.x, kFinishWaves);
 }
 
 // ----------------------------------------------------------------------------
@@ -1497,8 +1560,14 @@ hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream
   return wtype == 0 ? launch_step_w<0>(BB, a, grid, s) : launch_step_w<1>(BB, a, grid, s);
 }
 
-hipError_t launch_finish(const WalkArgs& a, int grid, hipStream_t s) {
-  finish_kernel<<<1, kFinishWaves * 64, 0, s>>>(a, grid);
+hipError_t launch_finish(const WalkArgs& a, hipStream_t s) {
+  finish_kernel<<<1, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s) {
+  const int pairs = a.B * a.gamma;
+  lse_kernel<<<(pairs + kLseWaves - 1) / kLseWaves, kLseWaves * 64, 0, s>>>(a, grid);
   return hipGetLastError();
 }
 

@@ -303,9 +303,11 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
       a.step = t;
       e = launch_step(ctx->wtype, BB, a, grid, s);
     }
-    if (e == hipSuccess) e = launch_finish(a, grid, s);
+    if (e == hipSuccess) e = launch_finish(a, s);
+    if (e == hipSuccess && a.lse) e = launch_lse(a, grid, s);
   } else {
     e = launch_walk(ctx->wtype, BB, a, ctx->grid, lds_bytes, ctx->cooperative, s);
+    if (e == hipSuccess && a.lse) e = launch_lse(a, ctx->grid, s);
   }
   if (e != hipSuccess) return WTS_ERR_DEVICE;
   ctx->walks++;

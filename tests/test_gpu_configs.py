@@ -161,3 +161,33 @@ def test_last_row_start_and_reuse_across_walks():
     for _ in range(3):   # the control block alternates parities walk after walk
         assert_exact(run(h, t), ref, "reuse")
     h.close()
+
+
+# ---- other residency points (Fig. 14 full case; int8 at the 248k vocabulary) ----
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_bf16_v151936_fully_resident(B):
+    # bf16 W at V = 151,936 (77.8 MB) stays on chip: 8 register + 2 LDS tiles per wave
+    d = datagen.make_inputs(151936, 256, B, 16, wtype="bf16", seed=41)
+    _case(test="bf16_v151936_resident", B=B, gamma=16)
+    h, t = make_head(d)
+    p = h.plan(B)
+    assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 151936 * 512, p
+    got = run(h, t)
+    assert_bf16_close(got, oracle_walk(d, keep_z=True), f"bf16 152k B={B}")
+    stream = run(h, t, exec="stream")
+    assert np.array_equal(stream["logits"], got["logits"]) and np.array_equal(stream["tokens"], got["tokens"])
+    h.close()
+
+
+@pytest.mark.parametrize("B,T", [(1, 0), (1, 1), (4, 0)])
+def test_int8_v248320_fully_resident_exact(B, T):
+    # int8 W at V = 248,320 (63.6 MB) stays on chip: registers, then LDS
+    d = datagen.make_inputs(248320, 256, B, 16, seed=42)
+    _case(test="int8_v248320_resident", B=B, gamma=16, T=T)
+    h, t = make_head(d)
+    p = h.plan(B, temperature=T)
+    assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 248320 * 256, p
+    got = run(h, t, temperature=T, seed=6)
+    assert_exact(got, oracle_walk(d, temperature=T, seed=6), f"int8 248k B={B} T={T}")
+    h.close()
