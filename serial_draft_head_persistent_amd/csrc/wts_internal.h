@@ -22,7 +22,7 @@ constexpr int waves_for(int head, int wtype) { return (head == 0 && wtype == 1) 
 // batches need more registers for latents and keys, so they keep fewer tiles
 // in registers and more in LDS.
 constexpr int reg_tiles_max(int head, int wtype, int BB) {
-  return wtype == 0 ? (BB <= 2 ? 5 : BB == 4 ? 4 : BB == 8 ? 3 : 2)
+  return wtype == 0 ? (BB == 1 ? 5 : BB <= 4 ? 4 : BB == 8 ? 3 : 2)
                     : waves_for(head, wtype) == 4 ? (BB == 1 ? 8 : BB == 2 ? 7 : BB <= 8 ? 6 : 5) : 1;
 }
 constexpr int kChunksI8 = 4;      // 16-byte lane chunks per int8 tile (64 k each)

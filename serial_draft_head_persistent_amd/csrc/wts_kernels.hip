@@ -403,16 +403,17 @@ __device__ __forceinline__ unsigned long long readlane(unsigned long long x, int
 }
 
 // 1 KiB of zeros in device memory: the A-operand source of the lanes whose
-// row is not in the slot being loaded.
+// A row holds no batch row of this walk.
 __device__ __attribute__((aligned(64))) int4 g_zero_page[64];
 
-// Latent of this step as MFMA A operands.  Slot s holds the latent rows in A
-// rows [s*RPS, (s+1)*RPS) and zeros elsewhere: every lane loads each slot's
-// 16-byte chunks either from its latent row (its own slot) or from the zero
-// page (other slots), so building the operands costs loads, not VALU work.
+// Latent of this step as MFMA A operands: lane l holds A row (l & 15) -- the
+// latent row (batch row, and hi or lo half for int8) of result row
+// (l & 15) % RPS -- and k chunk (l >> 4) of every 64-k (int8) or 32-k (bf16)
+// step.  Every slot of RPS A rows holds the same latent rows, so one operand
+// serves the S tiles of a group, each with its own accumulator.
 template <int WT, int BB, int HEAD>
 __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, BB>& ro, const int* sx,
-                                            const char* lds, v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH]) {
+                                            const char* lds, v4i (&lat)[Geo<WT, BB>::NM][Geo<WT, BB>::CH]) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m) {
@@ -423,32 +424,22 @@ __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, B
       const int x = ok ? sx[b] : 0;
       const v4i* src = WT == 0 ? (const v4i*)(a.Eq + (size_t)x * 512 + hl * 256 + ro.q * 16)
                                : (const v4i*)(a.Eb + (size_t)x * kR + ro.q * 8);
-      const v4i* zero = (const v4i*)g_zero_page;
+      const v4i* p = ok ? src : (const v4i*)g_zero_page;
 #pragma unroll
-      for (int s = 0; s < Gm::S; ++s) {
-        const v4i* p = (ok && ro.aslot == s) ? src : zero;
-#pragma unroll
-        for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = p[c * 4];
-      }
+      for (int c = 0; c < Gm::CH; ++c) lat[m][c] = p[c * 4];
     } else {
       const char* src = WT == 0 ? lds + kOffLat + (b * 2 + hl) * 256 + ro.q * 16
                                 : lds + kOffLat + (b * kR + ro.q * 8) * 2;
-      v4i d[Gm::CH];
 #pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) d[c] = ok ? *(const v4i*)(src + c * 64) : v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < Gm::S; ++s)
-#pragma unroll
-        for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = (ro.aslot == s) ? d[c] : v4i{0, 0, 0, 0};
+      for (int c = 0; c < Gm::CH; ++c) lat[m][c] = ok ? *(const v4i*)(src + c * 64) : v4i{0, 0, 0, 0};
     }
   }
 }
 
-// Same A operands as load_latent, from the candidate rows staged in LDS:
-// the own slot reads the winner's staged row, the other slots the LDS zeros.
+// Same A operands as load_latent, from the candidate rows staged in LDS.
 template <int WT, int BB>
 __device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Roles<WT, BB>& ro, const char* lds,
-                                                   v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH]) {
+                                                   v4i (&lat)[Geo<WT, BB>::NM][Geo<WT, BB>::CH]) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m) {
@@ -456,14 +447,25 @@ __device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Role
     const bool ok = b < a.B;
     const int slot = ok ? ((const int*)(lds + kOffWin))[b] : 0;
     const char* src = lds + kOffRows + slot * kRowBytes + ro.arow_hl(m) * 256 + ro.q * 16;
-    const char* zero = lds + kOffZero;
+    const char* p = ok ? src : lds + kOffZero;
 #pragma unroll
-    for (int s = 0; s < Gm::S; ++s) {
-      const char* p = (ok && ro.aslot == s) ? src : zero;
-#pragma unroll
-      for (int c = 0; c < Gm::CH; ++c) Aop[m][s][c] = *(const v4i*)(p + c * 64);
-    }
+    for (int c = 0; c < Gm::CH; ++c) lat[m][c] = *(const v4i*)(p + c * 64);
   }
+}
+
+// Result of this lane's tile in a group: accumulator s holds tile s of the
+// group in every lane; the lanes of result slot s (l >> 4 in slot s) take it.
+// (Bit masks rather than selects, so that the accumulators stay in registers
+// instead of becoming a dynamically indexed array.)
+template <int S, class AT>
+__device__ __forceinline__ AT pick_slot(const AT (&acc)[S], int cslot) {
+  v4i r = {0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int mask = -(int)(cslot == s);
+    r |= __builtin_bit_cast(v4i, acc[s]) & v4i{mask, mask, mask, mask};
+  }
+  return __builtin_bit_cast(AT, r);
 }
 
 // ---- per-step log normaliser of the logits (optional output) ----
@@ -624,7 +626,7 @@ template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
                                              TileBuf<WT, BB> cur,
-                                             const v4i (&Aop)[Geo<WT, BB>::NM][Geo<WT, BB>::S][Geo<WT, BB>::CH],
+                                             const v4i (&lat)[Geo<WT, BB>::NM][Geo<WT, BB>::CH],
                                              const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                              typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                              LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
@@ -644,8 +646,8 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
       AT acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
       for (int c = 0; c < Gm::CH; ++c) {
-        if (WT == 0 && (c & 1)) acc2 = mma(Aop[m][0][c], cur.w[c], acc2);
-        else acc = mma(Aop[m][0][c], cur.w[c], acc);
+        if (WT == 0 && (c & 1)) acc2 = mma(lat[m][c], cur.w[c], acc2);
+        else acc = mma(lat[m][c], cur.w[c], acc);
       }
       if (WT == 0) acc = acc + acc2;
       epilogue<WT, BB, TEMP, NZ, LS>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, ls, noise, row0);
@@ -1140,7 +1142,8 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   int* sx = (int*)(lds + kOffX);
   int* sflag = (int*)(lds + kOffFlag);
 
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile counts and branches stay scalar
   const Roles<WT, BB> ro(tid & 63);
   const int g = blockIdx.x, G = gridDim.x;
   const int tb = (int)((long long)g * a.tiles / G);
@@ -1275,11 +1278,11 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     // first non-register tile of this step: its load overlaps the register tiles' work
     TileBuf<WT, BB> first;
     if (nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
-    v4i Aop[Gm::NM][Gm::S][Gm::CH];
+    v4i lat[Gm::NM][Gm::CH];
     if (CAND && t > 0)
-      load_latent_staged<WT, BB>(a, ro, lds, Aop);
+      load_latent_staged<WT, BB>(a, ro, lds, lat);
     else
-      load_latent<WT, BB, HEAD>(a, ro, sx, lds, Aop);
+      load_latent<WT, BB, HEAD>(a, ro, sx, lds, lat);
     if (a.trace) {
       __builtin_amdgcn_s_waitcnt(0);
       stamp(t, 1);
@@ -1298,23 +1301,40 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
       if (gi * Gm::S < nreg) {
 #pragma unroll
         for (int m = 0; m < Gm::NM; ++m) {
-          // int8: two independent accumulator chains (even / odd chunks), summed
-          // exactly at the end; bf16 keeps one chain (the fp32 order of every
-          // execution mode is the same: chunk 0..7 per tile).
-          AT acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
-          const bool full = (gi + 1) * Gm::S <= nreg;
+          // One accumulator per tile of the group (independent MFMA chains).
+          // A single-tile int8 group splits its chunks over two chains, summed
+          // exactly at the end; bf16 keeps one chain per tile (the fp32 order
+          // of every execution mode is the same: chunk 0..7 per tile).
+          AT accs[Gm::S], acc2 = {0, 0, 0, 0};
+          constexpr bool SPLIT = WT == 0 && Gm::S == 1;
 #pragma unroll
-          for (int s = 0; s < Gm::S; ++s) {
-            const int i = gi * Gm::S + s;
-            if (i < Gm::RT && (full || i < nreg)) {
+          for (int s = 0; s < Gm::S; ++s) accs[s] = AT{0, 0, 0, 0};
+          if ((gi + 1) * Gm::S <= nreg && (gi + 1) * Gm::S <= Gm::RT) {
+            // a full group: chunk-major over its S tiles
 #pragma unroll
-              for (int c = 0; c < Gm::CH; ++c) {
-                if (WT == 0 && (c & 1)) acc2 = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc2);
-                else acc = mma(Aop[m][s][c], wr[i < Gm::RT ? i : 0][c], acc);
+            for (int c = 0; c < Gm::CH; ++c)
+#pragma unroll
+              for (int s = 0; s < Gm::S; ++s) {
+                const int i = gi * Gm::S + s < Gm::RT ? gi * Gm::S + s : 0;
+                if (SPLIT && (c & 1)) acc2 = mma(lat[m][c], wr[i][c], acc2);
+                else accs[s] = mma(lat[m][c], wr[i][c], accs[s]);
+              }
+          } else {
+            // the last, partial group: its first tiles, one after another
+#pragma unroll
+            for (int s = 0; s < Gm::S; ++s) {
+              const int i = gi * Gm::S + s;
+              if (i < Gm::RT && i < nreg) {
+#pragma unroll
+                for (int c = 0; c < Gm::CH; ++c) {
+                  if (SPLIT && (c & 1)) acc2 = mma(lat[m][c], wr[i < Gm::RT ? i : 0][c], acc2);
+                  else accs[s] = mma(lat[m][c], wr[i < Gm::RT ? i : 0][c], accs[s]);
+                }
               }
             }
           }
-          if (WT == 0) acc = acc + acc2;
+          AT acc = pick_slot<Gm::S>(accs, ro.cslot);
+          if (SPLIT) acc = acc + acc2;
           epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0),
                                             gok[gi], gsw[gi], bnx[gi][m], shi, best, ls, noise, row0);
         }
@@ -1322,7 +1342,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     }
     // LDS-resident and streamed tiles
     if (nreg < nw)
-      stream_tiles<WT, BB, TEMP, NW, NOISE, LS>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, Aop, shi, best, ls,
+      stream_tiles<WT, BB, TEMP, NW, NOISE, LS>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best, ls,
                                                 noise);
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
@@ -1425,8 +1445,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
       const int b = ro.bent(m, e);
       shi[m][e] = (WT == 0 && b < BB && b < a.B) ? a.Es[sx[b]] : 0.0f;
     }
-  v4i Aop[Gm::NM][Gm::S][Gm::CH];
-  load_latent<WT, BB, kHeadMarkov>(a, ro, sx, nullptr, Aop);
+  v4i lat[Gm::NM][Gm::CH];
+  load_latent<WT, BB, kHeadMarkov>(a, ro, sx, nullptr, lat);
   typename LKey<TEMP>::T best[Gm::NM][Gm::NE];
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m)
@@ -1437,7 +1457,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   if (nw > 0) {
     TileBuf<WT, BB> first;
     fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
-    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, Aop, shi, best,
+    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, lat, shi, best,
                                                       ls, (const float*)nullptr);
   }
   reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
