@@ -823,12 +823,44 @@ __device__ __forceinline__ unsigned long long ld_agent(const unsigned long long*
 __device__ __forceinline__ void st_agent(unsigned long long* p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Signalling inside one XCD through its shared L2: a plain store (the CU's
+// L1 writes through to the L2) and a non-temporal load, which the L1 does not
+// serve from a retained line.  About 0.28 us one way on MI355X, against
+// 0.47 us for the device-scope pair above, which bypasses the L2.
+__device__ __forceinline__ void st_xcd(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// N such loads in flight at once, then one wait.
+template <int N>
+__device__ __forceinline__ void ld_xcd(const unsigned long long* const (&p)[N], unsigned long long (&v)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 loads");
+  if constexpr (N == 1) {
+    asm volatile("global_load_dwordx2 %0, %1, off nt\n\ts_waitcnt vmcnt(0)" : "=v"(v[0]) : "v"(p[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "global_load_dwordx2 %0, %2, off nt\n\tglobal_load_dwordx2 %1, %3, off nt\n\ts_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(p[0]), "v"(p[1])
+        : "memory");
+  } else {
+    asm volatile(
+        "global_load_dwordx2 %0, %4, off nt\n\tglobal_load_dwordx2 %1, %5, off nt\n\t"
+        "global_load_dwordx2 %2, %6, off nt\n\tglobal_load_dwordx2 %3, %7, off nt\n\ts_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+  }
+}
 
 // Clear the control arrays of the next walk (parity par ^ 1), spread over
-// the whole grid.  Nothing in this walk touches them.
+// the whole grid.  Nothing in this walk touches them.  OWN_L1: each
+// workgroup clears its own first-level lines (the persistent walk, whose
+// first level stays inside an XCD); otherwise the grid clears all of them.
+template <bool OWN_L1>
 __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
   const int q = par ^ 1;
-  const size_t n1 = sizeof(ctrl->l1[0]) / 8, n2 = sizeof(ctrl->l2[0]) / 8, n3 = sizeof(ctrl->ss[0]) / 8;
+  if (OWN_L1 && threadIdx.x < 2 * kMaxB) ctrl->l1[q][threadIdx.x / kMaxB][blockIdx.x][threadIdx.x % kMaxB] = 0ull;
+  const size_t n1 = OWN_L1 ? 0 : sizeof(ctrl->l1[0]) / 8, n2 = sizeof(ctrl->l2[0]) / 8, n3 = sizeof(ctrl->ss[0]) / 8;
   unsigned long long* p1 = &ctrl->l1[q][0][0][0];
   unsigned long long* p2 = &ctrl->l2[q][0][0][0][0];
   unsigned long long* p3 = &ctrl->ss[q][0][0][0];
@@ -845,10 +877,15 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
 // the step, in its own line; the first workgroup of each of kGroups groups
 // waits for its members' keys and publishes the group maximum in kCopies
 // copies; every workgroup waits for the kGroups group maxima in copy
-// (g % kCopies) -- the copy read by the workgroups of its XCD under the
-// round-robin dispatch -- and takes the overall maximum.  The keys carry the token, so no other data has to be made
-// visible: relaxed device-scope loads and stores suffice.  Returns false if
-// the watchdog expired.  On return, lanes b < B hold the winning key of row b.
+// (g % kCopies) and takes the overall maximum.  Workgroups are dispatched
+// round-robin over the XCDs (g % 8 on MI355X), so a group (g % kGroups) lies
+// on one XCD: its keys travel through that XCD's L2 (st_xcd / ld_xcd), and
+// only the group maxima cross XCDs (device scope, one copy per XCD).  Were a
+// member on another XCD, its leader would not see the key and the watchdog
+// would latch a timeout; a stale line never passes for a new one, since every
+// key carries its step.  The keys carry the token, so no other data has to be
+// made visible: relaxed loads and stores suffice.  Returns false if the
+// watchdog expired.  On return, lanes b < B hold the winning key of row b.
 template <int BB, bool CAND>
 __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsigned long long key,
                                          long long timeout, unsigned long long* winner, char* lds) {
@@ -858,24 +895,34 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
   const unsigned long long tag = want << kTagShift;
   unsigned long long* L1 = &ctrl->l1[par][t & 1][0][0];
   unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0][0];
-  if (lane < B) st_agent(&L1[g * kMaxB + lane], tag | key);
+  if (lane < B) st_xcd(&L1[g * kMaxB + lane], tag | key);
   const int grp = g % kGroups;
   const long long t0 = wall_clock64();
   bool ok_all = true;
   if (g < kGroups) {
-    const int nmem = (G - grp + kGroups - 1) / kGroups;
+    const int nmem = (G - grp + kGroups - 1) / kGroups;  // at most kGroups members (G <= 256)
+    // member keys of this lane: entries q = lane + 64 k, member q / BB, row q % BB
+    constexpr int NQ = (kGroups * BB + 63) / 64;
+    const unsigned long long* pp[NQ];
+    bool act[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int q = lane + 64 * k, i = q / BB, b = q % BB;
+      act[k] = q < nmem * BB && b < B;
+      pp[k] = act[k] ? &L1[(grp + kGroups * i) * kMaxB + b] : &L1[g * kMaxB];  // idle lanes: own line
+    }
     unsigned long long best;
     while (true) {
+      unsigned long long v[NQ];
+      ld_xcd<NQ>(pp, v);
       bool ok = true;
       best = 0ull;
-      for (int q = lane; q < nmem * BB; q += 64) {
-        const int i = q / BB, b = q % BB;
-        if (b < B) {
-          const unsigned long long v = ld_agent(&L1[(grp + kGroups * i) * kMaxB + b]);
-          ok = ok && (v >> kTagShift) == want;
-          best = umax64(best, v);
+#pragma unroll
+      for (int k = 0; k < NQ; ++k)
+        if (act[k]) {
+          ok = ok && (v[k] >> kTagShift) == want;
+          best = umax64(best, v[k]);
         }
-      }
       if (__all(ok)) break;
       if (wall_clock64() - t0 > timeout) {
         ok_all = false;
@@ -1165,7 +1212,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
   char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
 
-  clear_next_walk(ctrl, par);
+  clear_next_walk<true>(ctrl, par);
 
   // One-time shard load (Fig. 4 entry cost): register tiles, then LDS tiles.
   v4i wr[Gm::RT][Gm::CH];
@@ -1415,7 +1462,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   const int t = a.step;
   Ctrl* ctrl = a.ctrl;
   const int par = a.parity;
-  if (t == 0) clear_next_walk(ctrl, par);
+  if (t == 0) clear_next_walk<false>(ctrl, par);
   if (tid < a.B) {
     int x = a.x0[tid];
     if (t > 0) {
