@@ -872,6 +872,30 @@ __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
   }
 }
 
+// Rotation by N lanes inside each 16-lane DPP row (row_ror), 64-bit.
+template <int N>
+__device__ __forceinline__ unsigned long long row_ror64(unsigned long long x) {
+  return ((unsigned long long)WTS_DPP((uint32_t)(x >> 32), 0x120 + N) << 32) | WTS_DPP((uint32_t)x, 0x120 + N);
+}
+
+// Maximum over the lanes that hold the same batch row (lane % BB) among the
+// first 16 * BB lanes; every lane of those rows ends with its class maximum.
+// DPP inside the 16-lane rows (the whole row for BB = 1, rotations by
+// multiples of BB otherwise), then across rows.
+template <int BB>
+__device__ __forceinline__ unsigned long long class_max(unsigned long long x) {
+  if constexpr (BB == 1) {
+    return row_max(x);  // 16 entries: one row
+  } else {
+    if constexpr (BB <= 8) x = kmax(x, row_ror64<BB>(x));
+    if constexpr (BB <= 4) x = kmax(x, row_ror64<2 * BB>(x));
+    if constexpr (BB <= 2) x = kmax(x, row_ror64<4 * BB>(x));
+    x = kmax(x, shfl_xor_u64(x, 16));
+    if constexpr (BB >= 4) x = kmax(x, shfl_xor_u64(x, 32));
+    return x;
+  }
+}
+
 // Cross-workgroup selection of one step (Fig. 8), one wave per workgroup.
 // Every workgroup publishes its local winner key per batch row, tagged with
 // the step, in its own line; the first workgroup of each of kGroups groups
@@ -929,10 +953,9 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
         break;
       }
     }
-#pragma unroll
-    for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
+    best = class_max<BB>(best);
     if (ok_all) {
-      // after the butterfly every lane holds the maximum of row (lane % BB)
+      // after class_max every lane holds the maximum of batch row (lane % BB)
       for (int q = lane; q < kCopies * BB; q += 64) {
         const int r = q / BB, b = q % BB;
         if (b < B) st_agent(&L2[(r * kGroups + grp) * kMaxB + b], best);
@@ -959,8 +982,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     if (__all(ok)) break;
     if (wall_clock64() - t0 > timeout) ok_all = false;
   }
-#pragma unroll
-  for (int m = BB; m < 64; m <<= 1) best = umax64(best, shfl_xor_u64(best, m));
+  best = class_max<BB>(best);
   *winner = best & kKeyMask;
   if (CAND && lane == 0)
     __hip_atomic_store((int*)(lds + kOffDone), ok_all ? t + 1 : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
