@@ -102,7 +102,7 @@ def fit_steps(head, d, t, gammas=(1, 7, 16), n=100, warmup=10, **kw):
 
 WALLCLOCK_MHZ = 100.0   # s_memrealtime rate on MI355X (hipDeviceAttributeWallClockRate)
 COPY_BYTES = 512 << 20  # the --copy-calib copy
-HEADLINE_KERNEL = "walk_kernel<0, 1, 0, 0, false>"
+HEADLINE_KERNEL = "walk_kernel<0, 1, 0, 0, false, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_traffic.json")
 
 

@@ -268,16 +268,17 @@ __global__ void bf16_rows_kernel(const float* __restrict__ E, long long n, uint1
 
 // Geometry of one (W type, batch bucket).  The A operand carries LPB latent
 // rows per batch row (hi and lo for int8, one for bf16).  With RPS latent
-// rows per slot, S = 16 / RPS tiles share one accumulator.
-template <int WT, int BB, int HD = 0>
+// rows per slot, S = 16 / RPS tiles share one A operand, each with its own
+// accumulator, and the lanes of result slot s take tile s.
+template <int WT, int BB, int HD = 0, bool FL = false>
 struct Geo {
   static constexpr int LPB = WT == 0 ? 2 : 1;
   static constexpr int ROWS = LPB * BB;
   static constexpr int NM = ROWS > 16 ? ROWS / 16 : 1;
-  static constexpr int RPS = WT == 0 ? (ROWS <= 4 ? 4 : (ROWS <= 8 ? 8 : 16)) : 16;
+  static constexpr int RPS = ROWS <= 4 ? 4 : (ROWS <= 8 ? 8 : 16);
   static constexpr int S = 16 / RPS;
   static constexpr int CH = WT == 0 ? kChunksI8 : kChunksBF;
-  static constexpr int RT = reg_tiles_max(HD, WT, BB);
+  static constexpr int RT = FL ? reg_tiles_full(HD, WT, BB) : reg_tiles_max(HD, WT, BB);
   static constexpr int NG = (RT + S - 1) / S;
   static constexpr int NE = 4 / LPB;  // batch entries per lane and M block
 };
@@ -575,11 +576,14 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
   }
 }
 
-// Base logits of one result entry set (bf16 bits), zero where unused.
+// Base logits of one result entry set (bf16 bits), zero where unused.  The
+// row index is made opaque so that the per-lane addresses are recomputed at
+// every step instead of being kept in registers for the whole walk.
 template <int WT, int BB>
 __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                           int v, bool ok, uint32_t (&bv)[Geo<WT, BB>::NE]) {
   using Gm = Geo<WT, BB>;
+  asm volatile("" : "+v"(v));
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
     const int b = ro.bent(m, e);
@@ -1199,11 +1203,13 @@ __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned 
 
 // The whole walk in one persistent launch: grid = one workgroup per CU.
 // LS: also the per-step log normaliser of the logits (lse output).
-template <int WT, int BB, int HEAD, int TEMP, bool LS>
+// FULL: the whole shard is on chip (more register tiles, no streaming; each
+// wave's LDS tiles follow the previous waves' in LDS).
+template <int WT, int BB, int HEAD, int TEMP, bool LS, bool FULL>
 __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkArgs a) {
   constexpr int NW = waves_for(HEAD, WT);
   constexpr int NT = NW * 64;
-  using Gm = Geo<WT, BB, HEAD>;
+  using Gm = Geo<WT, BB, HEAD, FULL>;
   using AT = typename AccT<WT>::T;
   constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1220,7 +1226,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   const int cnt = te - tb;
   const int nw = cnt > w ? (cnt - w + NW - 1) / NW : 0;
   const int nreg = min(nw, a.reg_tiles);
-  const int nlds = min(nw - nreg, a.lds_tiles);
+  const int nlds = FULL ? min(nw - nreg, kFullLdsMax) : min(nw - nreg, a.lds_tiles);
   Ctrl* ctrl = a.ctrl;
   const int par = a.parity;
   constexpr bool CAND = stage_candidates(HEAD, WT, BB);
@@ -1232,7 +1238,15 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   float2* lraw = lred + kWaves * kMaxB;                           // [entries][64]
   int* lcnt = (int*)(lds + kOffLseCnt);
   const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
-  char* ldsw = lds + scratch + (size_t)w * a.lds_tiles * TB;
+  int lds_before = w * a.lds_tiles;  // LDS tiles of the waves before this one
+  if (FULL) {
+    lds_before = 0;
+    for (int u = 0; u < w; ++u) {
+      const int nu = cnt > u ? (cnt - u + NW - 1) / NW : 0;
+      lds_before += nu - min(nu, a.reg_tiles);
+    }
+  }
+  char* ldsw = lds + scratch + (size_t)lds_before * TB;
 
   clear_next_walk<true>(ctrl, par);
 
@@ -1249,17 +1263,18 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
 #pragma unroll
     for (int c = 0; c < Gm::CH; ++c) *(v4i*)(ldsw + (size_t)i * TB + c * 1024 + ro.lane * 16) = p[c * 64];
   }
-  int gv[Gm::NG];
-  float gsw[Gm::NG];
-  bool gok[Gm::NG];
+  // vocabulary row of this lane's result in register group gi, and whether it exists
+  // (opaque to the compiler, so that values derived from it are recomputed at
+  // every step rather than held in registers for the whole walk)
+  auto gv = [&](int gi) {
+    int v = (tb + w + NW * (gi * Gm::S + ro.cslot)) * kTileRows + ro.n;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto gok = [&](int gi) { return gi * Gm::S + ro.cslot < nreg && gv(gi) < a.V; };
+  float gsw[WT == 0 ? Gm::NG : 1];  // row scales of the register groups (int8)
 #pragma unroll
-  for (int gi = 0; gi < Gm::NG; ++gi) {
-    const int i = gi * Gm::S + ro.cslot;
-    const int tile = tb + w + NW * i;
-    gv[gi] = tile * kTileRows + ro.n;
-    gok[gi] = i < nreg && gv[gi] < a.V;
-    gsw[gi] = (WT == 0 && gok[gi]) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
-  }
+  for (int gi = 0; gi < (WT == 0 ? Gm::NG : 1); ++gi) gsw[gi] = (WT == 0 && gok(gi)) ? a.sw[gv(gi)] : 0.0f;
   const int row0 = tb * kTileRows;  // first vocabulary row of this workgroup
   float* noise_lds = NOISE ? (float*)(lds + a.noise_off) : nullptr;
   const float* noise = noise_lds;
@@ -1313,11 +1328,26 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   // tile are loaded one step ahead, so their memory latency overlaps the
   // previous step's exchange.
   uint32_t bnx[Gm::NG][Gm::NM][Gm::NE];
+  // FULL: LDS tiles in slot groups like the register tiles, base logits loaded ahead
+  constexpr int NLG = FULL ? (kFullLdsMax + Gm::S - 1) / Gm::S : 1;
+  auto lv = [&](int gl) {
+    int v = (tb + w + NW * (nreg + gl * Gm::S + ro.cslot)) * kTileRows + ro.n;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto lok = [&](int gl) { return gl * Gm::S + ro.cslot < nlds && lv(gl) < a.V; };
+  uint32_t bnl[NLG][Gm::NM][Gm::NE];
   auto fetch_base = [&](int t) {
 #pragma unroll
     for (int gi = 0; gi < Gm::NG; ++gi)
 #pragma unroll
-      for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, gv[gi], gok[gi], bnx[gi][m]);
+      for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, gv(gi), gok(gi), bnx[gi][m]);
+    if (FULL) {
+#pragma unroll
+      for (int gl = 0; gl < NLG; ++gl)
+#pragma unroll
+        for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, lv(gl), lok(gl), bnl[gl][m]);
+    }
   };
   fetch_base(0);
 
@@ -1346,7 +1376,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
       }
     // first non-register tile of this step: its load overlaps the register tiles' work
     TileBuf<WT, BB> first;
-    if (nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
+    if (!FULL && nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i lat[Gm::NM][Gm::CH];
     if (CAND && t > 0)
       load_latent_staged<WT, BB>(a, ro, lds, lat);
@@ -1404,15 +1434,42 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
           }
           AT acc = pick_slot<Gm::S>(accs, ro.cslot);
           if (SPLIT) acc = acc + acc2;
-          epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, acc, gv[gi], 0xFFFFu - (uint32_t)(gv[gi] - row0),
-                                            gok[gi], gsw[gi], bnx[gi][m], shi, best, ls, noise, row0);
+          epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
+                                            gok(gi), WT == 0 ? gsw[gi] : 0.0f, bnx[gi][m], shi, best, ls,
+                                            noise, row0);
         }
       }
     }
     // LDS-resident and streamed tiles
-    if (nreg < nw)
+    if (FULL) {
+      // LDS tiles only, S per group, their chunks read straight into the MFMA operands
+#pragma unroll
+      for (int gl = 0; gl < NLG; ++gl) {
+        if (gl * Gm::S < nlds) {
+          __builtin_amdgcn_sched_barrier(0);  // one group's chunks in flight at a time (registers)
+#pragma unroll
+          for (int m = 0; m < Gm::NM; ++m) {
+            AT accs[Gm::S];
+#pragma unroll
+            for (int s = 0; s < Gm::S; ++s) accs[s] = AT{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < Gm::CH; ++c)
+#pragma unroll
+              for (int s = 0; s < Gm::S; ++s)
+                if (gl * Gm::S + s < nlds)
+                  accs[s] = mma(lat[m][c], *(const v4i*)(ldsw + (size_t)(gl * Gm::S + s) * TB + c * 1024 +
+                                                          ro.lane * 16), accs[s]);
+            const int v = lv(gl);
+            epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, pick_slot<Gm::S>(accs, ro.cslot), v,
+                                              0xFFFFu - (uint32_t)(v - row0), lok(gl), 0.0f, bnl[gl][m], shi,
+                                              best, ls, noise, row0);
+          }
+        }
+      }
+    } else if (nreg < nw) {
       stream_tiles<WT, BB, TEMP, NW, NOISE, LS>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best, ls,
                                                 noise);
+    }
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
     // Fig. 8: local winner -> device-scope max key and arrival count -> wait
@@ -1589,7 +1646,9 @@ hipError_t launch_bf16_rows(const float* E, int V, uint16_t* Eb, hipStream_t s) 
 template <int WT, int BB, int HEAD, int TEMP, bool LS>
 static hipError_t launch_walk_t(const WalkArgs& a, int grid, int lds_bytes, bool coop, hipStream_t s) {
   void* args[] = {(void*)&a};
-  const void* fn = (const void*)walk_kernel<WT, BB, HEAD, TEMP, LS>;
+  const void* fn = (const void*)walk_kernel<WT, BB, HEAD, TEMP, LS, false>;
+  if constexpr (reg_tiles_full(HEAD, WT, BB) > 0)
+    if (a.full) fn = (const void*)walk_kernel<WT, BB, HEAD, TEMP, LS, true>;
   const dim3 blk(waves_for(HEAD, WT) * 64);
   if (coop) return hipLaunchCooperativeKernel(fn, dim3(grid), blk, args, (unsigned)lds_bytes, s);
   return hipLaunchKernel(fn, dim3(grid), blk, args, (size_t)lds_bytes, s);
@@ -1663,11 +1722,17 @@ hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s) {
 template <int WT, int HEAD, int TEMP, bool LS>
 static hipError_t set_lds_attr(int lds_bytes) {
   hipError_t e = hipSuccess;
-  const void* fns[] = {(const void*)walk_kernel<WT, 1, HEAD, TEMP, LS>, (const void*)walk_kernel<WT, 2, HEAD, TEMP, LS>,
-                       (const void*)walk_kernel<WT, 4, HEAD, TEMP, LS>, (const void*)walk_kernel<WT, 8, HEAD, TEMP, LS>,
-                       (const void*)walk_kernel<WT, 16, HEAD, TEMP, LS>};
+  const void* fns[] = {
+      (const void*)walk_kernel<WT, 1, HEAD, TEMP, LS, false>, (const void*)walk_kernel<WT, 2, HEAD, TEMP, LS, false>,
+      (const void*)walk_kernel<WT, 4, HEAD, TEMP, LS, false>, (const void*)walk_kernel<WT, 8, HEAD, TEMP, LS, false>,
+      (const void*)walk_kernel<WT, 16, HEAD, TEMP, LS, false>};
   for (const void* f : fns) {
     const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (r != hipSuccess) e = r;
+  }
+  if constexpr (reg_tiles_full(HEAD, WT, 1) > 0) {
+    const hipError_t r = hipFuncSetAttribute((const void*)walk_kernel<WT, 1, HEAD, TEMP, LS, true>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (r != hipSuccess) e = r;
   }
   return e;

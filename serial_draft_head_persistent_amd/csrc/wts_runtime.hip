@@ -68,9 +68,13 @@ int noise_floats(const wts_ctx* ctx, int BB, int temperature) {
   return per_wg * kTileRows;
 }
 
-// Residency plan for one batch bucket.
+// Tiles wave w of a workgroup with cnt tiles owns (every NW-th tile).
+int wave_tiles(int cnt, int w, int NW) { return cnt > w ? (cnt - w + NW - 1) / NW : 0; }
+
+// Residency plan for one batch bucket.  *full: the whole shard fits on chip
+// in the variant with more register tiles and LDS tiles allotted per wave.
 void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* p, int* lds_bytes,
-               int* noise_off = nullptr, int* noise_stride = nullptr) {
+               int* noise_off = nullptr, int* noise_stride = nullptr, int* full = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
   const int NW = waves_for(ctx->head, ctx->wtype);
   const int per_wave = (per_wg + NW - 1) / NW;
@@ -86,27 +90,42 @@ void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* 
   lds = std::min(lds, per_wave - reg);
   if (ctx->lds_cap >= 0) lds = std::min(lds, ctx->lds_cap);
   if (exec != WTS_EXEC_RESIDENT) reg = lds = 0;
+  bool whole = false;
+  int lds_need = NW * lds;  // LDS tiles of the fullest workgroup
+  const int regf = std::min(reg_tiles_full(ctx->head, ctx->wtype, BB), per_wave);
+  if (regf > 0 && exec == WTS_EXEC_RESIDENT && ctx->reg_cap < 0 && ctx->lds_cap < 0 && reg + lds < per_wave) {
+    int need = 0, most = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int rest = wave_tiles(per_wg, w, NW) - std::min(wave_tiles(per_wg, w, NW), regf);
+      need += rest;
+      most = std::max(most, rest);
+    }
+    if (need * tb <= kLdsMax - scratch && most <= kFullLdsMax) {
+      whole = true;
+      reg = regf;
+      lds = most;
+      lds_need = need;
+    }
+  }
+  if (full) *full = whole ? 1 : 0;
   p->grid = ctx->grid;
   p->waves = NW;
   p->tiles = ctx->tiles;
   p->tiles_per_wave = per_wave;
   p->reg_tiles = reg;
   p->lds_tiles = lds;
-  p->stream_tiles = per_wave - reg - lds;
+  p->stream_tiles = whole ? 0 : per_wave - reg - lds;
   // exact on-chip bytes: count each wave's tiles
   long long res_tiles = 0;
   for (int g = 0; g < ctx->grid; ++g) {
     const int cnt = (int)((long long)(g + 1) * ctx->tiles / ctx->grid) - (int)((long long)g * ctx->tiles / ctx->grid);
-    for (int w = 0; w < NW; ++w) {
-      const int nw = cnt > w ? (cnt - w + NW - 1) / NW : 0;
-      res_tiles += std::min(nw, reg + lds);
-    }
+    for (int w = 0; w < NW; ++w) res_tiles += whole ? wave_tiles(cnt, w, NW) : std::min(wave_tiles(cnt, w, NW), reg + lds);
   }
   const long long esz = ctx->wtype == WTS_W_INT8 ? 1 : 2;
   p->w_bytes = (long long)ctx->V * kR * esz;
   p->resident_bytes = res_tiles * tb;
   p->streamed_bytes = (long long)ctx->tiles * tb - p->resident_bytes;
-  *lds_bytes = std::min(kLdsMax, std::max(scratch + NW * lds * tb, 96 * 1024));
+  *lds_bytes = std::min(kLdsMax, std::max(scratch + lds_need * tb, 96 * 1024));
 }
 
 template <class T>
@@ -255,8 +274,8 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   const int BB = batch_bucket(p->B);
   wts_plan plan;
   int lds_bytes = 0;
-  int noise_off = 0, noise_stride = 0;
-  make_plan(ctx, BB, p->exec, p->temperature, &plan, &lds_bytes, &noise_off, &noise_stride);
+  int noise_off = 0, noise_stride = 0, full = 0;
+  make_plan(ctx, BB, p->exec, p->temperature, &plan, &lds_bytes, &noise_off, &noise_stride, &full);
 
   WalkArgs a{};
   a.Wp = ctx->Wp;
@@ -291,6 +310,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.trace = (long long*)p->trace_out;
   a.timeout_ticks = ctx->timeout_ticks;
   a.fixed_latent = (p->flags & WTS_WALK_FIXED_LATENT) != 0;
+  a.full = full;
   a.lse = p->lse_out;
   a.lse_part = ctx->lse_part;
   hipStream_t s = (hipStream_t)p->stream;

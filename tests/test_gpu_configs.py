@@ -102,7 +102,11 @@ def test_config3_bf16_tolerance(B):
     ds["base"], ds["x0"] = d["base"][:B], d["x0"][:B]
     h, t = make_head(d)
     p = h.plan(B)
-    assert p["stream_tiles"] > 0                  # 248k bf16 is partially resident
+    if B == 1:
+        # one batch row: the whole 127 MB bf16 shard on chip (11 register tiles per wave + LDS)
+        assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 248320 * 512, p
+    else:
+        assert p["stream_tiles"] > 0              # more batch rows: partially resident
     ts = dict(t)
     ts["base"], ts["x0"] = t["base"][:B].contiguous(), t["x0"][:B].contiguous()
     got = run(h, ts)
@@ -190,4 +194,23 @@ def test_int8_v248320_fully_resident_exact(B, T):
     assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 248320 * 256, p
     got = run(h, t, temperature=T, seed=6)
     assert_exact(got, oracle_walk(d, temperature=T, seed=6), f"int8 248k B={B} T={T}")
+    h.close()
+
+
+@pytest.mark.parametrize("T", [0, 1])
+def test_bf16_v248320_whole_shard_matches_streaming(T):
+    # the whole-shard-on-chip kernel and the streaming kernel give identical bits
+    # (same fp32 order per tile); the oracle bar as in the config test
+    d = cached_inputs(3, B=1, gamma=8)
+    _case(test="bf16_248k_whole_vs_stream", T=T)
+    h, t = make_head(d)
+    assert h.plan(1, temperature=T)["stream_tiles"] == 0
+    got = run(h, t, temperature=T, seed=3, lse=True)
+    stream = run(h, t, exec="stream", temperature=T, seed=3, lse=True)
+    assert np.array_equal(got["tokens"], stream["tokens"]) and np.array_equal(got["logits"], stream["logits"])
+    assert np.allclose(got["lse"], stream["lse"], rtol=1e-5, atol=0)
+    assert_bf16_close(got, oracle_walk(d, temperature=T, seed=3, keep_z=True), f"bf16 248k whole T={T}")
+    probe = run(h, t, temperature=T, seed=3, fixed_latent=True)
+    assert_bf16_close(probe, oracle_walk(d, temperature=T, seed=3, keep_z=True, fixed_latent=True),
+                      f"bf16 248k whole probe T={T}")
     h.close()
