@@ -1118,11 +1118,25 @@ __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, con
     float ps[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) ps[i] = 0.0f;
-#pragma unroll 4
-    for (int kb = 0; kb < kR / 8; ++kb) {
-      const uint4 w8 = A8[kb * kR + j];
-      const float4 h0 = *(const float4*)(h + b * kR + kb * 8);
-      const float4 h1 = *(const float4*)(h + b * kR + kb * 8 + 4);
+    // LDS loads run two k-blocks ahead of the arithmetic
+    constexpr int KB = kR / 8, D = BB >= 16 ? 1 : 2;
+    uint4 wq[D + 1];
+    float4 hq0[D + 1], hq1[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      wq[d] = A8[d * kR + j];
+      hq0[d] = *(const float4*)(h + b * kR + d * 8);
+      hq1[d] = *(const float4*)(h + b * kR + d * 8 + 4);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb + D < KB) {
+        wq[(kb + D) % (D + 1)] = A8[(kb + D) * kR + j];
+        hq0[(kb + D) % (D + 1)] = *(const float4*)(h + b * kR + (kb + D) * 8);
+        hq1[(kb + D) % (D + 1)] = *(const float4*)(h + b * kR + (kb + D) * 8 + 4);
+      }
+      const uint4 w8 = wq[kb % (D + 1)];
+      const float4 h0 = hq0[kb % (D + 1)], h1 = hq1[kb % (D + 1)];
       ps[0] = ps[0] + __uint_as_float(w8.x << 16) * h0.x;
       ps[1] = ps[1] + __uint_as_float(w8.x & 0xFFFF0000u) * h0.y;
       ps[2] = ps[2] + __uint_as_float(w8.y << 16) * h0.z;
