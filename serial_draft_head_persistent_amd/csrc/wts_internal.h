@@ -47,10 +47,11 @@ constexpr int kLdsMax = 163840;
 constexpr int kHeadMarkov = 0;
 constexpr int kHeadRecurrent = 1;
 
-// Int8 Markov walks of one batch row stage the embedding rows of the
-// exchange's candidates (the group maxima) in LDS while the exchange runs.
+// Walks of one batch row stage the embedding rows of the exchange's
+// candidates (the group maxima) in LDS while the exchange runs: int8 Markov
+// walks (E_q rows) and recurrent walks (fp32 E rows).
 constexpr bool stage_candidates(int head, int wtype, int BB) {
-  return head == kHeadMarkov && wtype == 0 && BB == 1;
+  return BB == 1 && (head == kHeadRecurrent || wtype == 0);
 }
 // LDS bytes in front of the LDS-resident W tiles.
 constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
@@ -61,7 +62,7 @@ constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
 // [result entries][64], at most 2 KiB; 1 KiB at B=1), in a part of the
 // scratch that nothing else of that kernel uses.
 constexpr int lse_lds_offset(int head, int wtype, int BB) {
-  return head == kHeadRecurrent ? 26624 : stage_candidates(head, wtype, BB) ? 18688 : 2048;
+  return head == kHeadRecurrent ? (BB == 1 ? 29696 : 26624) : stage_candidates(head, wtype, BB) ? 18688 : 2048;
 }
 
 constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most

@@ -206,10 +206,21 @@ __global__ void repack_bf16_kernel(const uint16_t* __restrict__ W, int V, int ti
 }
 
 // Wave-wide maximum of a float (all lanes get the result).
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+// Maximum of a non-negative float over the wave: DPP maxima inside each
+// 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror), then the four rows via readlane.  For x >= 0 the bit patterns
+// order as the values do.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t b = __float_as_uint(x);
+#define WTS_QMAX(c) b = max(b, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, (c), 0xF, 0xF, false))
+  WTS_QMAX(0xB1);
+  WTS_QMAX(0x4E);
+  WTS_QMAX(0x141);
+  WTS_QMAX(0x140);
+#undef WTS_QMAX
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)b, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)b, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)b, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)b, 48);
+  return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
 // Two-int8-vector latent of one 256-vector held 4 values per lane (Fig. 7):
@@ -218,7 +229,7 @@ __device__ __forceinline__ float wave_max(float x) {
 // s_lo = s_hi / 256.  Returns s_hi; hi/lo of elements 4*lane..+3 in *hi,*lo.
 __device__ __forceinline__ float quant4(const float u[4], uint32_t* hi4, uint32_t* lo4) {
   float amax = fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3])));
-  amax = wave_max(amax);
+  amax = wave_max_nonneg(amax);
   uint32_t ph = 0, pl = 0;
   float s_hi = 0.0f;
   if (amax != 0.0f) {
@@ -299,6 +310,8 @@ constexpr int kOffShs = kOffRows + kGroups * 2 * kRowBytes;  // float [kGroups *
 constexpr int kOffLat = 2048;                     // int8 [kMaxB][2][256] or bf16 [kMaxB][256]
 constexpr int kOffH = kOffLat + kMaxB * 512;       // float [kMaxB][256]
 constexpr int kOffAt = 32768;                      // recurrent: A bf16 as [k/8][256 j][8]
+constexpr int kOffRecRows = 12288;                 // recurrent, one batch row: staged fp32 E rows [kGroups]
+constexpr int kRecRowBytes = kR * 4;
 
 
 __device__ __forceinline__ v4i mma(const v4i& a, const v4i& b, const v4i& c) {
@@ -999,7 +1012,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
 // nothing waits for it inside the loop).  When the exchange is done, record
 // which staged row holds the winner of each batch row (the largest candidate
 // key) and wait for the copies.  The next step builds its latent from LDS.
-template <int BB>
+template <int HEAD, int BB>
 __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, long long timeout) {
   typedef __attribute__((address_space(3))) void lds_void;
   const int lane = threadIdx.x & 63;
@@ -1038,11 +1051,17 @@ __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, 
         }
       const int v = key_token(kc & kKeyMask);
       if (!better || v < 0 || v >= a.V) continue;
-      if (lane < 32)
-        __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
-                                         (lds_void*)(lds + kOffRows + c * kRowBytes), 16, 0, 0);
-      if (lane == 0)
-        __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + c * 4), 4, 0, 0);
+      if (HEAD == kHeadMarkov) {
+        if (lane < 32)
+          __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
+                                           (lds_void*)(lds + kOffRows + c * kRowBytes), 16, 0, 0);
+        if (lane == 0)
+          __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + c * 4), 4, 0, 0);
+      } else {
+        // the fp32 row, 16 bytes per lane
+        __builtin_amdgcn_global_load_lds((const void*)(a.E + (size_t)v * kR + lane * 4),
+                                         (lds_void*)(lds + kOffRecRows + c * kRecRowBytes), 16, 0, 0);
+      }
     }
   };
   const long long t0 = wall_clock64();
@@ -1063,16 +1082,20 @@ __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, 
 // Recurrent head, first half of a step (Fig. 13): h_{t+1} = tanh(A h_t +
 // E[x_t] + c) with the A h_t sums (ascending k) already in acc; then the
 // latent rows for the projection (int8 hi/lo + s_hi, or bf16) into LDS.
+// staged: E[x_t] is the candidate row staged in LDS during the exchange.
 template <int WT, int BB>
 __device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, const int* sx, char* lds,
-                                                  const float (&racc)[BB], float cj) {
+                                                  const float (&racc)[BB], float cj, bool staged) {
   float* h = (float*)(lds + kOffH);
   if (tid >= kThreads - kR) {
     const int j = tid - (kThreads - kR);
 #pragma unroll
     for (int b = 0; b < BB; ++b)
       if (b < a.B) {
-        const float pre = (racc[b] + a.E[(size_t)sx[b] * kR + j]) + cj;
+        const float e = staged ? ((const float*)(lds + kOffRecRows + ((const int*)(lds + kOffWin))[b] *
+                                                            kRecRowBytes))[j]
+                               : a.E[(size_t)sx[b] * kR + j];
+        const float pre = (racc[b] + e) + cj;
         h[b * kR + j] = tanh_p(pre);
       }
   }
@@ -1099,9 +1122,9 @@ __device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, co
 }
 
 // Recurrent head: racc[b] = sum_k A[j][k] h[b][k] in binary32 as eight
-// interleaved partial sums (k mod 8, ascending k in each) combined as
-// ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)): eight independent add chains per
-// thread.  A lives in LDS as [k/8][j][8] bf16, so thread j reads the eight
+// interleaved partial sums (k mod 8, ascending k in each, one fused
+// multiply-add per term) combined as ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)):
+// eight independent chains per thread.  A lives in LDS as [k/8][j][8] bf16, so thread j reads the eight
 // weights of a k-block with one 16-byte load; h is read as a broadcast.
 template <int BB>
 __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, const char* lds, float (&racc)[BB]) {
@@ -1137,14 +1160,14 @@ __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, con
       }
       const uint4 w8 = wq[kb % (D + 1)];
       const float4 h0 = hq0[kb % (D + 1)], h1 = hq1[kb % (D + 1)];
-      ps[0] = ps[0] + __uint_as_float(w8.x << 16) * h0.x;
-      ps[1] = ps[1] + __uint_as_float(w8.x & 0xFFFF0000u) * h0.y;
-      ps[2] = ps[2] + __uint_as_float(w8.y << 16) * h0.z;
-      ps[3] = ps[3] + __uint_as_float(w8.y & 0xFFFF0000u) * h0.w;
-      ps[4] = ps[4] + __uint_as_float(w8.z << 16) * h1.x;
-      ps[5] = ps[5] + __uint_as_float(w8.z & 0xFFFF0000u) * h1.y;
-      ps[6] = ps[6] + __uint_as_float(w8.w << 16) * h1.z;
-      ps[7] = ps[7] + __uint_as_float(w8.w & 0xFFFF0000u) * h1.w;
+      ps[0] = fmaf(__uint_as_float(w8.x << 16), h0.x, ps[0]);
+      ps[1] = fmaf(__uint_as_float(w8.x & 0xFFFF0000u), h0.y, ps[1]);
+      ps[2] = fmaf(__uint_as_float(w8.y << 16), h0.z, ps[2]);
+      ps[3] = fmaf(__uint_as_float(w8.y & 0xFFFF0000u), h0.w, ps[3]);
+      ps[4] = fmaf(__uint_as_float(w8.z << 16), h1.x, ps[4]);
+      ps[5] = fmaf(__uint_as_float(w8.z & 0xFFFF0000u), h1.y, ps[5]);
+      ps[6] = fmaf(__uint_as_float(w8.w << 16), h1.z, ps[6]);
+      ps[7] = fmaf(__uint_as_float(w8.w & 0xFFFF0000u), h1.w, ps[7]);
     }
     racc[b] = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
   }
@@ -1329,7 +1352,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   __syncthreads();
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
-  if (CAND && fixed) {
+  if (HEAD == kHeadMarkov && CAND && fixed) {
     // the probe's latent, staged once where later steps read staged rows
     if (tid < kRowBytes / 16) ((int4*)(lds + kOffRows))[tid] = ((const int4*)(a.Eq + (size_t)sx[0] * 512))[tid];
     if (tid == 0) {
@@ -1372,7 +1395,8 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   for (int t = 0; t < a.gamma; ++t) {
     stamp(t, 0);
     // state -> latent (Markov: embedding row of x_t; recurrent: h_{t+1})
-    if (HEAD == kHeadRecurrent && (t == 0 || !fixed)) recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj);
+    if (HEAD == kHeadRecurrent && (t == 0 || !fixed))
+      recurrent_advance<WT, BB>(a, tid, sx, lds, racc, cj, stage && t > 0);
     // scales of the latent rows (int8), issued with the latent gather
     float shi[Gm::NM][Gm::NE];
 #pragma unroll
@@ -1382,7 +1406,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         const int b = ro.bent(m, e);
         shi[m][e] = 0.0f;
         if (WT == 0 && b < BB && b < a.B) {
-          if (CAND && t > 0)
+          if (HEAD == kHeadMarkov && CAND && t > 0)
             shi[m][e] = ((const float*)(lds + kOffShs))[((const int*)(lds + kOffWin))[b]];
           else
             shi[m][e] = HEAD == kHeadMarkov ? a.Es[sx[b]] : ((const float*)(lds + kOffShi))[b];
@@ -1392,7 +1416,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     TileBuf<WT, BB> first;
     if (!FULL && nreg < nw) fetch_tile<WT, BB, NW>(a, ro, t, tb, w, nreg, nreg, nlds, ldsw, first);
     v4i lat[Gm::NM][Gm::CH];
-    if (CAND && t > 0)
+    if (HEAD == kHeadMarkov && CAND && t > 0)
       load_latent_staged<WT, BB>(a, ro, lds, lat);
     else
       load_latent<WT, BB, HEAD>(a, ro, sx, lds, lat);
@@ -1495,7 +1519,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     // the workgroup's log-sum-exp pairs of this step, merged during the exchange
     if (w > 0) lse_workgroup<WT, BB, NW, LS>(a, ro, w, ls, lred, lraw, lcnt, t, g, G);
     if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
-    if (stage && w == 1 && t + 1 < a.gamma) stage_rows<BB>(a, t, lds, a.timeout_ticks);
+    if (stage && w == 1 && t + 1 < a.gamma) stage_rows<HEAD, BB>(a, t, lds, a.timeout_ticks);
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
       make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);

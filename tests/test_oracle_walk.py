@@ -53,8 +53,8 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0, fixed=False):
                 hn = []
                 for j in range(r):
                     ps = [Fraction(0)] * 8   # eight interleaved partial sums, fixed tree
-                    for k in range(r):
-                        ps[k % 8] = rnd32(ps[k % 8] + rnd32(_F(A[j, k]) * _F(h[k])))
+                    for k in range(r):       # one fused multiply-add per term
+                        ps[k % 8] = rnd32(ps[k % 8] + _F(A[j, k]) * _F(h[k]))
                     acc = rnd32(rnd32(rnd32(ps[0] + ps[1]) + rnd32(ps[2] + ps[3]))
                                 + rnd32(rnd32(ps[4] + ps[5]) + rnd32(ps[6] + ps[7])))
                     pre = rnd32(rnd32(acc + _F(E[x, j])) + _F(d["c"][j]))
@@ -336,3 +336,26 @@ def test_walk_lse_is_normaliser_of_its_logits():
     for b in range(2):
         for t in range(4):
             assert o["lse"][b, t] == log_normaliser(o["logits"][b, t])
+
+
+def test_fma32_exact_against_rationals():
+    # RN32(a b + c) with a bf16-valued, b and c binary32: against exact rationals,
+    # including sums that cancel almost completely and exact ties
+    rng = np.random.default_rng(27)
+    n = 20000
+    a = bf16_to_f32(bf16_rne(rng.normal(0, 1, n).astype(np.float32)))
+    b = rng.normal(0, 1, n).astype(np.float32)
+    c = rng.normal(0, 1, n).astype(np.float32)
+    c[: n // 4] = (-(a[: n // 4].astype(np.float64) * b[: n // 4]).astype(np.float32))  # near cancellation
+    c[n // 4: n // 2] *= np.float32(2.0 ** -30)                                          # tiny addend
+    got = oracle.fma32(a, b, c)
+    for i in range(0, n, 7):
+        want = rnd32(_F(a[i]) * _F(b[i]) + _F(c[i]))
+        assert Fraction(float(got[i])) == want, (a[i], b[i], c[i])
+    # ties: a b + c exactly halfway between two binary32 values
+    one = np.float32(1.0)
+    half_ulp = np.float32(2.0 ** -24)
+    got = oracle.fma32(np.array([one, one], np.float32), np.array([one, np.float32(1.0 + 2.0 ** -23)], np.float32),
+                       np.array([half_ulp, half_ulp], np.float32))
+    assert got[0] == np.float32(1.0)                      # 1 + 2^-24 ties to even (1)
+    assert got[1] == np.float32(1.0 + 2.0 ** -22)         # 1 + 2^-23 + 2^-24 ties to even (up)
