@@ -2,9 +2,9 @@
 
 Test infrastructure only (see ``oracle/__init__``).
 
-The pages state that the projection result is "rounded once to bf16"
-(Weights That Stay, Fig. 7).  bf16 here is the upper 16 bits of an IEEE
-binary32 value, rounded to nearest even.
+Weights That Stay, Fig. 7: the projection result is rounded to bf16 a single
+time.  bf16 here is the upper 16 bits of an IEEE binary32 value, rounded to
+nearest even.
 
 log_p / exp_p / tanh_p are *specifications* of the elementary functions used
 by T=1 Gumbel noise (Fig. 10, bottom row) and by the recurrent head's tanh

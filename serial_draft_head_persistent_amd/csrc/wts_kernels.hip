@@ -4,32 +4,36 @@
 // Speculative Decoding" (arXiv 2611.00506).  One persistent launch runs the
 // whole gamma-step walk (Fig. 1, Fig. 4): each workgroup keeps its shard of
 // the vocabulary projection W on chip, projects the step's latent through it,
-// selects a local winner, and all workgroups agree on the common winner
-// through a 64-bit atomic maximum plus an arrival count (Fig. 8) before the
-// state advances in the kernel.  int8 W uses the two-int8-vector latent of
-// Fig. 7; bf16 W uses the latent rounded to bf16.
+// selects a local winner, all workgroups agree on the common winner (Fig. 8),
+// and the state advances in the kernel.  int8 W uses the two-int8-vector
+// latent of Fig. 7; bf16 W uses the latent rounded to bf16.
 //
 // MI355X mapping (not the pages' H100/B200 design):
-//  * one workgroup of 8 waves per CU; a wave owns every 8th 16-row tile of
-//    its workgroup's contiguous tile range;
+//  * one workgroup per CU, of 8 waves (4 for bf16 Markov walks, which need a
+//    whole SIMD's register file per wave); a wave owns every NW-th 16-row tile
+//    of its workgroup's contiguous tile range;
 //  * a tile is one MFMA N block: the latent rows are the A operand (16 x K),
 //    the 16 vocabulary rows of the tile the B operand (K x 16), so the
 //    projection of a step is a chain of v_mfma_i32_16x16x64_i8 (int8 W) or
 //    v_mfma_f32_16x16x32_bf16 (bf16 W) per tile;
-//  * when the batch leaves latent rows unused, several tiles share one MFMA
-//    accumulator by placing the latent in different A rows ("slots"), so all
-//    64 lanes of the result carry useful logits;
-//  * W tiles live in VGPRs (registers), then LDS, and the remainder streams
-//    from HBM each step with one tile of prefetch;
+//  * when the batch leaves A rows unused, the A operand repeats the latent
+//    rows in every slot of RPS rows, S tiles run against it with their own
+//    accumulators, and the lanes of result slot s take tile s, so all 64 lanes
+//    of the result carry useful logits;
+//  * W tiles live in registers, then LDS, and the remainder streams from HBM
+//    each step with one tile of prefetch; a whole-shard variant (bf16, one
+//    batch row) drops the streaming buffers to hold more tiles in registers;
 //  * the cross-workgroup selection is a two-level all-gather of step-tagged
-//    64-bit keys through device memory (one line per workgroup, a group
-//    leader per 16 workgroups, one line per group), polled by one wave per
-//    workgroup with a wall-clock watchdog.  On MI355X a single-address atomic
-//    maximum plus an arrival counter serialises 2 x 256 device-scope atomics
-//    per step (measured ~11 us per step); the all-gather needs none.
+//    64-bit keys (one line per workgroup, a group leader per 16 workgroups,
+//    one line per group and XCD), polled by one wave per workgroup with a
+//    wall-clock watchdog.  The first level stays inside one XCD's L2.  Fig. 8
+//    has each worker atomically update one maximum and an arrival count; on
+//    MI355X that serialises 2 x 256 device-scope atomics per step (measured
+//    ~11 us per step), and the all-gather needs none.
 //
 // Bit-exactness with the host reference needs: no contraction of a*b+c
-// (built with -ffp-contract=off), IEEE division (default), rintf half-even.
+// (built with -ffp-contract=off; the recurrent sum's fused multiply-adds are
+// explicit fmaf calls), IEEE division (default), rintf half-even.
 
 #include "wts_internal.h"
 
@@ -43,8 +47,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // scalar helpers
 // ----------------------------------------------------------------------------
 
-// bf16 = upper half of binary32, rounded to nearest even (Fig. 7: "rounded
-// once to bf16").
+// bf16 = upper half of binary32, rounded to nearest even (Fig. 7: the
+// logit is rounded to bf16 a single time).
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   uint32_t b = __float_as_uint(x);
   b += 0x7FFFu + ((b >> 16) & 1u);
@@ -52,7 +56,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 }
 __device__ __forceinline__ float bf16_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Selection key (Fig. 8, "packs its local winner"): bits 49..18 order the
+// Selection key (Fig. 8: each worker's local winner as one key): bits 49..18 order the
 // binary32 scores (-0 folded into +0), bits 17..0 hold 0x3FFFF - v so the
 // lowest index wins among equal scores (V < 2^18).  0 is below every key.
 // Bits 63..57 are left free for the step tag of the cross-workgroup exchange.
