@@ -107,11 +107,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_traffic.json")
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank space removed, so
+    that the committed counters stay attached to the code they measured."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("wts_kernels.hip", "wts_internal.h"):
-        with open(os.path.join(ROOT, "serial_draft_head_persistent_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "serial_draft_head_persistent_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
