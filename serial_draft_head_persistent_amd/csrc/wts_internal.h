@@ -29,11 +29,11 @@ constexpr int reg_tiles_max(int head, int wtype, int BB) {
                     : waves_for(head, wtype) == 4 ? (BB == 1 ? 8 : BB == 2 ? 7 : BB <= 8 ? 6 : 5) : 1;
 }
 // Register tiles per wave of the whole-shard-on-chip variant (bf16 Markov
-// walks of one batch row): without streaming buffers a wave can hold more W
-// in registers, and LDS tiles are handed out per wave as needed, so the bf16
-// shard of a 248k vocabulary (61 tiles per CU) stays on chip.  0: no such
-// variant.  kFullLdsMax: LDS tiles a wave of that variant may own.
-constexpr int reg_tiles_full(int head, int wtype, int BB) { return (head == 0 && wtype == 1 && BB == 1) ? 11 : 0; }
+// walks of up to four batch rows): without streaming buffers a wave can hold
+// more W in registers, and LDS tiles are handed out per wave as needed, so
+// the bf16 shard of a 248k vocabulary (61 tiles per CU) stays on chip.  0: no
+// such variant.  kFullLdsMax: LDS tiles a wave of that variant may own.
+constexpr int reg_tiles_full(int head, int wtype, int BB) { return (head == 0 && wtype == 1 && BB <= 4) ? 11 : 0; }
 constexpr int kFullLdsMax = 6;
 constexpr int kChunksI8 = 4;      // 16-byte lane chunks per int8 tile (64 k each)
 constexpr int kChunksBF = 8;      // 16-byte lane chunks per bf16 tile (32 k each)

@@ -1773,9 +1773,13 @@ static hipError_t set_lds_attr(int lds_bytes) {
     if (r != hipSuccess) e = r;
   }
   if constexpr (reg_tiles_full(HEAD, WT, 1) > 0) {
-    const hipError_t r = hipFuncSetAttribute((const void*)walk_kernel<WT, 1, HEAD, TEMP, LS, true>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (r != hipSuccess) e = r;
+    const void* full[] = {(const void*)walk_kernel<WT, 1, HEAD, TEMP, LS, true>,
+                          (const void*)walk_kernel<WT, 2, HEAD, TEMP, LS, true>,
+                          (const void*)walk_kernel<WT, 4, HEAD, TEMP, LS, true>};
+    for (const void* f : full) {
+      const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (r != hipSuccess) e = r;
+    }
   }
   return e;
 }
