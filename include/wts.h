@@ -91,6 +91,10 @@ typedef struct wts_create_params {
                              holds CUs the walk fails with WTS_ERR_TIMEOUT
                              instead of hanging).  1: cooperative launch, which
                              guarantees co-residency at ~18 us more per walk. */
+  int32_t watchdog_us;    /* 0: 2 s.  Otherwise the wall-clock limit, in
+                             microseconds (>= 1), of every wait inside a walk;
+                             a wait that exceeds it latches WTS_ERR_TIMEOUT and
+                             its workgroup exits.                              */
 } wts_create_params;
 
 typedef struct wts_walk_params {

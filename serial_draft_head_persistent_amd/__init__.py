@@ -31,7 +31,7 @@ class Head:
     """
 
     def __init__(self, W, E, *, w_scale=None, A=None, c=None, head="markov", max_batch=16,
-                 max_steps=64, resident_tiles=-1, lds_tiles=-1, cooperative=False):
+                 max_steps=64, resident_tiles=-1, lds_tiles=-1, cooperative=False, watchdog_us=0):
         import torch
         self._torch = torch
         wtype = "int8" if W.dtype == torch.int8 else "bf16"
@@ -47,7 +47,8 @@ class Head:
         p = _abi.CreateParams(V=self.V, r=self.r, head=HEAD[head], wtype=WTYPE[wtype], W=_ptr(W),
                               w_scale=_ptr(w_scale), E=_ptr(E), A=_ptr(A), c=_ptr(c), max_batch=max_batch,
                               max_steps=max_steps, resident_tiles=resident_tiles, lds_tiles=lds_tiles,
-                              device=W.device.index or 0, cooperative=int(bool(cooperative)))
+                              device=W.device.index or 0, cooperative=int(bool(cooperative)),
+                              watchdog_us=watchdog_us)
         h = ctypes.c_void_p()
         _check(_abi.lib().wts_create(ctypes.byref(p), ctypes.byref(h)), "wts_create")
         self._h = h

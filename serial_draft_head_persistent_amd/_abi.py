@@ -27,7 +27,8 @@ class CreateParams(ctypes.Structure):
     _fields_ = [("V", c_int32), ("r", c_int32), ("head", c_int32), ("wtype", c_int32),
                 ("W", c_void_p), ("w_scale", c_void_p), ("E", c_void_p), ("A", c_void_p), ("c", c_void_p),
                 ("max_batch", c_int32), ("max_steps", c_int32), ("resident_tiles", c_int32),
-                ("lds_tiles", c_int32), ("device", c_int32), ("cooperative", c_int32)]
+                ("lds_tiles", c_int32), ("device", c_int32), ("cooperative", c_int32),
+                ("watchdog_us", c_int32)]
 
 
 class WalkParams(ctypes.Structure):

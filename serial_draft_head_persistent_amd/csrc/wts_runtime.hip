@@ -192,6 +192,7 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
     return WTS_ERR_DEVICE;
   if (cus < 1 || (p->cooperative && !coop)) return WTS_ERR_UNSUPPORTED;
   if (p->cooperative != 0 && p->cooperative != 1) return WTS_ERR_INVALID_ARG;
+  if (p->watchdog_us < 0) return WTS_ERR_INVALID_ARG;
 
   wts_ctx* ctx = new (std::nothrow) wts_ctx();
   if (!ctx) return WTS_ERR_NO_MEMORY;
@@ -209,7 +210,9 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   ctx->E = p->E;
   ctx->A = p->A;
   ctx->c = p->c;
-  ctx->timeout_ticks = (long long)clock_khz * 1000LL * 2;  // 2 s per barrier wait
+  // per wait: 2 s, or the caller's limit (the wall clock runs at clock_khz kHz)
+  ctx->timeout_ticks = p->watchdog_us ? std::max(1LL, (long long)clock_khz * p->watchdog_us / 1000LL)
+                                      : (long long)clock_khz * 1000LL * 2;
 
   const size_t tb = tile_bytes(p->wtype);
   wts_status st = dmalloc(&ctx->Wp, (size_t)ctx->tiles * tb);

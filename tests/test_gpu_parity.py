@@ -90,3 +90,25 @@ def test_x0_out_of_range_is_latched():
     assert h.error() == "WTS_OK"
     assert_exact(run(h, t), oracle_walk(d), "after error")
     h.close()
+
+
+def test_watchdog_latches_timeout_and_grid_drains():
+    # A 1 us limit on every wait cannot hold one step's exchange (the last
+    # workgroup arrives ~0.5 us after the first, and a key needs ~0.8 us to
+    # cross both levels), so the walk latches WTS_ERR_TIMEOUT; every
+    # workgroup leaves its wait by itself and the launch completes.
+    import torch
+    d = cached_inputs(0)
+    _print_case(test="watchdog", watchdog_us=1)
+    h, t = make_head(d, watchdog_us=1)
+    h.walk(t["base"], t["x0"])
+    torch.cuda.synchronize()
+    assert h.error() == "WTS_ERR_TIMEOUT"
+    assert h.error() == "WTS_OK"
+    # the step-wise path has no waits inside a launch: it still runs on this context
+    assert_exact(run(h, t, exec="stepwise"), oracle_walk(d), "step-wise after time-out")
+    h.close()
+    # and a context with the default limit computes the walk
+    h2, t2 = make_head(d, t)
+    assert_exact(run(h2, t2), oracle_walk(d), "after time-out")
+    h2.close()
