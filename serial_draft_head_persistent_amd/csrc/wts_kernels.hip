@@ -873,6 +873,14 @@ __device__ __forceinline__ void ld_xcd(const unsigned long long* const (&p)[N], 
   }
 }
 
+// LDS address of a pointer into the workgroup's LDS, for hand-issued LDS
+// reads.  The compiler makes every LDS access it emits wait for all
+// outstanding global->LDS copies (it cannot tell which bytes they write); a
+// polling loop that starts such copies reads its LDS words by hand instead.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // Clear the control arrays of the next walk (parity par ^ 1), spread over
 // the whole grid.  Nothing in this walk touches them.  OWN_L1: each
 // workgroup clears its own first-level lines (the persistent walk, whose
@@ -1010,76 +1018,72 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
   return ok_all;
 }
 
-// Wave 1 during the exchange of step t (int8 Markov, B <= 2): as wave 0
-// publishes group maxima in LDS, copy each candidate's embedding row (hi | lo)
-// and its s_hi from memory straight into LDS (global_load_lds, no registers,
-// nothing waits for it inside the loop).  When the exchange is done, record
-// which staged row holds the winner of each batch row (the largest candidate
-// key) and wait for the copies.  The next step builds its latent from LDS.
+// Wave 1 during the exchange of step t (one batch row): as wave 0 publishes
+// group maxima in LDS, copy the embedding row of the largest candidate seen
+// so far (Markov: hi | lo and s_hi; recurrent: the fp32 row) from memory
+// straight into LDS (global_load_lds: no registers, nothing waits for it
+// inside the loop).  Every poll reduces all candidates at once (lane c holds
+// group c's key), so a new maximum starts its copy one LDS round trip after
+// wave 0 stores it; only a candidate larger than all earlier ones can win, so
+// the last row copied is the winner's once the exchange is complete.  Then
+// record which staged row that is and wait for the copies.  The next step
+// builds its latent from LDS.
 template <int HEAD, int BB>
 __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, long long timeout) {
+  static_assert(BB == 1, "one batch row: the group maxima are the lanes of DPP row 0");
   typedef __attribute__((address_space(3))) void lds_void;
   const int lane = threadIdx.x & 63;
   const int ngr = gridDim.x < kGroups ? gridDim.x : kGroups;
   const unsigned long long want = (unsigned long long)(t + 1);
-  const bool mine = lane < ngr * BB && (lane % BB) < a.B;  // lane = candidate (group lane/BB, row lane%BB)
-  unsigned long long* cand = (unsigned long long*)(lds + kOffCand);
-  unsigned long long seen = 0ull;  // wave-uniform bit set of candidates looked at
-  // Only a candidate larger than every earlier one of its batch row can win,
-  // so only those rows are copied; the last copied row of each batch row is
-  // the winner once the exchange is complete.
-  unsigned long long bestk[BB];
-  int bestc[BB];
-#pragma unroll
-  for (int b = 0; b < BB; ++b) {
-    bestk[b] = 0ull;
-    bestc[b] = b;
-  }
-  auto stage_new = [&]() {
-    const unsigned long long k =
-        mine ? __hip_atomic_load(cand + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
-    unsigned long long todo = __ballot(mine && (k >> kTagShift) == want) & ~seen;
-    seen |= todo;
-    while (todo) {
-      const int c = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const unsigned long long kc = readlane(k, c);
-      const int b = c % BB;
-      bool better = false;
-#pragma unroll
-      for (int bb = 0; bb < BB; ++bb)
-        if (bb == b && kc > bestk[bb]) {
-          bestk[bb] = kc;
-          bestc[bb] = c;
-          better = true;
-        }
-      const int v = key_token(kc & kKeyMask);
-      if (!better || v < 0 || v >= a.V) continue;
-      if (HEAD == kHeadMarkov) {
-        if (lane < 32)
-          __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
-                                           (lds_void*)(lds + kOffRows + c * kRowBytes), 16, 0, 0);
-        if (lane == 0)
-          __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + c * 4), 4, 0, 0);
-      } else {
-        // the fp32 row, 16 bytes per lane
-        __builtin_amdgcn_global_load_lds((const void*)(a.E + (size_t)v * kR + lane * 4),
-                                         (lds_void*)(lds + kOffRecRows + c * kRecRowBytes), 16, 0, 0);
-      }
+  const bool mine = lane < ngr;  // lane = candidate of group `lane`
+  const unsigned long long* cand = (const unsigned long long*)(lds + kOffCand);
+  unsigned long long bestk = 0ull;
+  int bestc = 0;
+  auto stage_new = [&](unsigned long long kl) {
+    const unsigned long long k = (mine && (kl >> kTagShift) == want) ? kl : 0ull;
+    const unsigned long long m = readlane(row_max(k), 0);  // lanes >= 16 hold no candidate
+    if (m <= bestk) return;
+    bestk = m;
+    bestc = __builtin_ctzll(__ballot(k == m));
+    const int v = key_token(m & kKeyMask);
+    if (v < 0 || v >= a.V) return;
+    if (HEAD == kHeadMarkov) {
+      if (lane < 32)
+        __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
+                                         (lds_void*)(lds + kOffRows + bestc * kRowBytes), 16, 0, 0);
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + bestc * 4), 4, 0, 0);
+    } else {
+      // the fp32 row, 16 bytes per lane
+      __builtin_amdgcn_global_load_lds((const void*)(a.E + (size_t)v * kR + lane * 4),
+                                       (lds_void*)(lds + kOffRecRows + bestc * kRecRowBytes), 16, 0, 0);
     }
   };
+  // Every lane reads its candidate word (lanes past the candidates read unused
+  // bytes below the rows) and the done flag, with one wait for both.
+  const uint32_t a_cand = lds_addr(cand + lane), a_done = lds_addr(lds + kOffDone);
+  auto poll = [&](unsigned long long& kl) {
+    int dn;
+    asm volatile("ds_read_b64 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(kl), "=&v"(dn)
+                 : "v"(a_cand), "v"(a_done)
+                 : "memory");
+    return __builtin_amdgcn_readfirstlane(dn);
+  };
   const long long t0 = wall_clock64();
-  while (true) {
-    const int dn = __hip_atomic_load((int*)(lds + kOffDone), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    stage_new();
+  for (int it = 1;; ++it) {
+    unsigned long long kl;
+    const int dn = poll(kl);
+    stage_new(kl);
     if (dn == t + 1 || dn == -1) break;
-    if (wall_clock64() - t0 > timeout) break;
+    if ((it & 7) == 0 && wall_clock64() - t0 > timeout) break;  // the watchdog, every 8 polls
   }
-  stage_new();  // candidates published in the last poll
-  if (lane == 0) {
-#pragma unroll
-    for (int b = 0; b < BB; ++b) ((int*)(lds + kOffWin))[b] = bestc[b];
+  {
+    unsigned long long kl;
+    poll(kl);
+    stage_new(kl);  // candidates published in the last poll
   }
+  if (lane == 0) ((int*)(lds + kOffWin))[0] = bestc;
   __builtin_amdgcn_s_waitcnt(0);  // the LDS copies are complete before the workgroup barrier
 }
 
@@ -1523,7 +1527,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     // the workgroup's log-sum-exp pairs of this step, merged during the exchange
     if (w > 0) lse_workgroup<WT, BB, NW, LS>(a, ro, w, ls, lred, lraw, lcnt, t, g, G);
     if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
-    if (stage && w == 1 && t + 1 < a.gamma) stage_rows<HEAD, BB>(a, t, lds, a.timeout_ticks);
+    if constexpr (CAND) {
+      if (stage && w == 1 && t + 1 < a.gamma) stage_rows<HEAD, BB>(a, t, lds, a.timeout_ticks);
+    }
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
       make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
