@@ -992,22 +992,34 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     }
   }
   const int ngr = G < kGroups ? G : kGroups;
+  // group maxima of this lane: entries q = lane + 64 k, group q / BB, row q % BB,
+  // all loads of a poll in flight at once
+  constexpr int NQ2 = (kGroups * BB + 63) / 64;
+  const unsigned long long* p2[NQ2];
+  bool act2[NQ2];
+#pragma unroll
+  for (int k = 0; k < NQ2; ++k) {
+    const int q = lane + 64 * k, x = q / BB, b = q % BB;
+    act2[k] = q < ngr * BB && b < B;
+    p2[k] = &L2[((g % kCopies) * kGroups + (act2[k] ? x : 0)) * kMaxB + (act2[k] ? b : 0)];
+  }
   unsigned long long best = 0ull;
   while (ok_all) {
+    unsigned long long v[NQ2];
+#pragma unroll
+    for (int k = 0; k < NQ2; ++k) v[k] = ld_agent(p2[k]);
     bool ok = true;
     best = 0ull;
-    for (int q = lane; q < ngr * BB; q += 64) {
-      const int x = q / BB, b = q % BB;
-      if (b < B) {
-        const unsigned long long v = ld_agent(&L2[((g % kCopies) * kGroups + x) * kMaxB + b]);
-        const bool here = (v >> kTagShift) == want;
+#pragma unroll
+    for (int k = 0; k < NQ2; ++k)
+      if (act2[k]) {
+        const bool here = (v[k] >> kTagShift) == want;
         ok = ok && here;
-        best = umax64(best, v);
+        best = umax64(best, v[k]);
         if (CAND && here)  // let wave 1 start staging this candidate's row
-          __hip_atomic_store((unsigned long long*)(lds + kOffCand) + q, v, __ATOMIC_RELAXED,
+          __hip_atomic_store((unsigned long long*)(lds + kOffCand) + lane + 64 * k, v[k], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-    }
     if (__all(ok)) break;
     if (wall_clock64() - t0 > timeout) ok_all = false;
   }
@@ -1184,12 +1196,13 @@ __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, con
 // Gumbel noise of step t for every (batch row, vocabulary row) of this
 // workgroup into LDS: one Philox4x32-10 call per group of four consecutive
 // rows (they share the counter and use its four output words), then
-// g = -log(-log U) per word.  Threads [first, first + count) share the work.
+// g = -log(-log U) per word.  count threads share the work; this one is
+// number idx among them.
 __device__ __forceinline__ void make_noise(const WalkArgs& a, float* noise, int t, int row0, int rows,
-                                           int first, int count) {
+                                           int idx, int count) {
   const int quads = rows >> 2;
   const int items = a.B * quads;
-  for (int it = (int)threadIdx.x - first; it < items; it += count) {
+  for (int it = idx; it < items; it += count) {
     const int b = it / quads, qd = it - b * quads;
     const int v0 = row0 + 4 * qd;
     uint32_t c0 = (uint32_t)v0 >> 2, c1 = (uint32_t)(a.step_offset + t), c2 = (uint32_t)b, c3 = 0u;
@@ -1356,7 +1369,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     for (int i = tid; i < a.B * kR; i += NT) h[i] = a.h0[i];
     if (tid >= kThreads - kR) cj = a.c[tid - (kThreads - kR)];
   }
-  if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, 0, NT);
+  if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, tid, NT);
   __syncthreads();
   if (*sflag) return;
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
@@ -1532,7 +1545,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     }
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
-      make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
+      make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, tid - (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
     if (w == 0) {
       const int lane = ro.lane;
       unsigned long long k = 0ull;

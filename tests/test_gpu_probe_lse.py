@@ -24,7 +24,7 @@ def _print_case(**kw):
 # ---- fixed-latent probe -------------------------------------------------------
 
 @pytest.mark.parametrize("exec_", ["resident", "stream", "stepwise"])
-@pytest.mark.parametrize("B", [1, 2, 5, 16])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 16])
 @pytest.mark.parametrize("T", [0, 1])
 def test_fixed_latent_markov_exact(exec_, B, T):
     d = datagen.make_inputs(4099, 256, B, 6, seed=31)
