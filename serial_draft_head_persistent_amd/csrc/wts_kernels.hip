@@ -1259,6 +1259,35 @@ __device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned 
   if (acc == 0x9E3779B9u) *lds_dummy = 1;  // keeps the loads; the byte is never read
 }
 
+// While wave 0 exchanges keys, other waves read one word of every 128-byte
+// line of the next step's base logits over this workgroup's rows.  The
+// non-register tiles load their base logits only one tile ahead of use; with
+// the lines already in the XCD's L2 those loads do not wait for memory.
+// At most two lines per thread (a hint: lines past that are not read).
+struct BaseTouch {
+  uint32_t v[2];
+};
+__device__ __forceinline__ BaseTouch touch_base(const WalkArgs& a, int t, int row0, int rows, int idx, int count) {
+  BaseTouch r{};
+  const int r1 = min(row0 + rows, a.V);
+  if (r1 > row0) {
+    const int nl = (r1 - row0 + 63) / 64 + 1;  // every 64th row (128 bytes apart), then the last row
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = idx + k * count;
+      if (q < a.B * nl) {
+        const int b = q / nl, l = q % nl;
+        const int v = l + 1 == nl ? r1 - 1 : row0 + 64 * l;
+        r.v[k] = a.base[((size_t)b * a.gamma + t) * a.V + v];
+      }
+    }
+  }
+  return r;
+}
+__device__ __forceinline__ void touch_done(const BaseTouch& r, char* lds_dummy) {
+  if ((r.v[0] ^ r.v[1]) == 0x9E37u) *lds_dummy = 1;  // keeps the loads; the byte is never read
+}
+
 // The whole walk in one persistent launch: grid = one workgroup per CU.
 // LS: also the per-step log normaliser of the logits (lse output).
 // FULL: the whole shard is on chip (more register tiles, no streaming; each
@@ -1543,9 +1572,16 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     if constexpr (CAND) {
       if (stage && w == 1 && t + 1 < a.gamma) stage_rows<HEAD, BB>(a, t, lds, a.timeout_ticks);
     }
+    // next step's base-logit lines into the L2 when some tiles are not in
+    // registers (greedy Markov walks; at T=1 these waves make the noise)
+    constexpr bool TOUCH = !FULL && !NOISE && HEAD == kHeadMarkov;
+    const bool touch = TOUCH && cnt > NW * a.reg_tiles && t + 1 < a.gamma && w >= (CAND ? 2 : 1);
+    BaseTouch bt{};
+    if (touch) bt = touch_base(a, t + 1, row0, cnt * kTileRows, tid - (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
     // next step's noise while wave 0 (and wave 1 when staging) waits on the exchange
     if (NOISE && t + 1 < a.gamma && w >= (CAND ? 2 : 1))
       make_noise(a, noise_lds, t + 1, row0, cnt * kTileRows, tid - (CAND ? 2 : 1) * 64, NT - (CAND ? 2 : 1) * 64);
+    if (touch) touch_done(bt, lds + kOffFlag + 4);
     if (w == 0) {
       const int lane = ro.lane;
       unsigned long long k = 0ull;
