@@ -604,7 +604,15 @@ __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
     const int b = ro.bent(m, e);
-    bv[e] = (b < BB && ok && b < a.B) ? (uint32_t)a.base[((size_t)b * a.gamma + t) * a.V + v] : 0u;
+    if (b >= BB) {  // compile-time: entry unused by this batch bucket
+      bv[e] = 0u;
+      continue;
+    }
+    // Every lane loads (element 0 where the pair does not exist; the epilogue
+    // drops such pairs), so the loads are straight-line code and nothing
+    // waits for them before their use.
+    const bool use = ok && b < a.B;
+    bv[e] = a.base[use ? ((size_t)b * a.gamma + t) * a.V + v : 0];
   }
 }
 
@@ -625,25 +633,31 @@ __device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB
   using Gm = Geo<WT, BB>;
   constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
   const int tile = tb + w + NWV * i;
+  // LDS and global pointers kept apart, so that the two branches stay LDS and
+  // global loads (one merged generic load would count against both wait
+  // counters and make every wait conservative)
+  typedef const __attribute__((address_space(3))) char lds_char;
+  typedef const __attribute__((address_space(1))) v4i glb_v4i;
   if (i < i0 + nlds) {
-    const char* p = ldsw + (size_t)(i - i0) * TB + ro.lane * 16;
+    lds_char* p = (lds_char*)(ldsw + (size_t)(i - i0) * TB + ro.lane * 16);
 #pragma unroll
-    for (int c = 0; c < Gm::CH; ++c) d.w[c] = *(const v4i*)(p + c * 1024);
+    for (int c = 0; c < Gm::CH; ++c) d.w[c] = *(const __attribute__((address_space(3))) v4i*)(p + c * 1024);
   } else {
-    const v4i* p = (const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane;
+    glb_v4i* p = (glb_v4i*)((const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane);
 #pragma unroll
     for (int c = 0; c < Gm::CH; ++c) d.w[c] = p[c * 64];
   }
   const int v = tile * kTileRows + ro.n;
   const bool ok = ro.cslot == 0 && v < a.V;
-  d.sw = (WT == 0 && ok) ? a.sw[tile * kTileRows + ro.n] : 0.0f;
+  d.sw = WT == 0 ? a.sw[ok ? v : 0] : 0.0f;  // every lane loads (see load_base)
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, d.bv[m]);
 }
 
 // Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), one tile of
-// prefetch.  `cur` holds tile i0 of this step, loaded before the step began.
-template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS>
+// prefetch.  `cur` holds tile i0 of this step, loaded before the step began
+// (a copy: its buffer is reused for the tiles after it).
+template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS, bool PP>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
                                              TileBuf<WT, BB> cur,
@@ -655,9 +669,7 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
   const int row0 = tb * kTileRows;
   using Gm = Geo<WT, BB>;
   using AT = typename AccT<WT>::T;
-  for (int i = i0; i < nw; ++i) {
-    TileBuf<WT, BB> nxt;
-    if (i + 1 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 1, i0, nlds, ldsw, nxt);
+  auto compute = [&](const TileBuf<WT, BB>& cur, int i) {
     const int tile = tb + w + NWV * i;
     const int v = tile * kTileRows + ro.n;
     const bool ok = ro.cslot == 0 && v < a.V;
@@ -673,7 +685,27 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
       if (WT == 0) acc = acc + acc2;
       epilogue<WT, BB, TEMP, NZ, LS>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, ls, noise, row0);
     }
-    if (i + 1 < nw) cur = nxt;
+  };
+  if constexpr (PP) {
+    // Two buffers used in turn: the next tile's loads go into the buffer that
+    // is not being computed, and nothing is copied from a buffer whose loads
+    // are still in flight (a copy would make the wave wait for them at once).
+    TileBuf<WT, BB> b1;
+    for (int i = i0; i < nw; i += 2) {
+      if (i + 1 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 1, i0, nlds, ldsw, b1);
+      compute(cur, i);
+      if (i + 1 >= nw) break;
+      if (i + 2 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 2, i0, nlds, ldsw, cur);
+      compute(b1, i + 1);
+    }
+  } else {
+    // one buffer and a copy (kernels without the registers for two)
+    for (int i = i0; i < nw; ++i) {
+      TileBuf<WT, BB> nxt;
+      if (i + 1 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 1, i0, nlds, ldsw, nxt);
+      compute(cur, i);
+      if (i + 1 < nw) cur = nxt;
+    }
   }
 }
 
@@ -1555,8 +1587,10 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         }
       }
     } else if (nreg < nw) {
-      stream_tiles<WT, BB, TEMP, NW, NOISE, LS>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best, ls,
-                                                noise);
+      // two tile buffers unless the registers are short (T=1 at sixteen int8 rows, recurrent at T=1)
+      constexpr bool PP = !(TEMP == 1 && (HEAD == kHeadRecurrent || (WT == 0 && BB >= 16)));
+      stream_tiles<WT, BB, TEMP, NW, NOISE, LS, PP>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best,
+                                                    ls, noise);
     }
     if (t + 1 < a.gamma) fetch_base(t + 1);
 
@@ -1680,8 +1714,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   if (nw > 0) {
     TileBuf<WT, BB> first;
     fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
-    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, lat, shi, best,
-                                                      ls, (const float*)nullptr);
+    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS, true>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, lat, shi,
+                                                            best, ls, (const float*)nullptr);
   }
   reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
   lse_reduce_to_lds<WT, BB, LS>(ro, w, ls, lred);
