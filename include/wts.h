@@ -167,6 +167,18 @@ wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t tem
 /* Static description of a status code. */
 const char* wts_status_string(wts_status s);
 
+/* Self-check of a numerical shortcut in the kernels.  A T=1 walk draws
+ * Gumbel noise -log(-log U) (Gumbel-max, Fig. 10) with a portable binary32
+ * log, which divides f by 2 + f for a reduced argument f = m - 1, m in
+ * [sqrt(1/2), sqrt(2)).  The kernels form that quotient from a reciprocal
+ * estimate and one fused-multiply-add correction instead of the general
+ * IEEE division.  This runs both on `device` for all 2^23 reduced mantissas
+ * and writes to *mismatches how many differ (0: the shortcut is the correctly
+ * rounded quotient everywhere the log can use it).  Allocates and frees 8
+ * bytes of device memory; synchronous.  WTS_ERR_INVALID_ARG for a NULL
+ * pointer or a negative device, WTS_ERR_DEVICE on a HIP error. */
+wts_status wts_check_log_ratio(int32_t device, int64_t* mismatches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,15 @@ import ctypes
 from . import _abi
 from ._abi import WtsError, EXEC, HEAD, WTYPE  # noqa: F401
 
-__all__ = ["Head", "WtsError"]
+__all__ = ["Head", "WtsError", "check_log_ratio"]
+
+
+def check_log_ratio(device=0):
+    """Mismatches between the kernels' log-argument quotient and the IEEE
+    division over every reduced argument (wts_check_log_ratio); 0 expected."""
+    n = ctypes.c_int64(-1)
+    _check(_abi.lib().wts_check_log_ratio(int(device), ctypes.byref(n)), "wts_check_log_ratio")
+    return n.value
 
 
 def _ptr(t):

@@ -18,7 +18,8 @@ WTYPE = {"int8": 0, "bf16": 1}
 EXEC = {"resident": 0, "stream": 1, "stepwise": 2}
 WALK_FIXED_LATENT = 1
 
-EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string"]
+EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string",
+           "wts_check_log_ratio"]
 
 c_int32, c_uint64, c_void_p = ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
 
@@ -78,6 +79,8 @@ def load(path=LIB_PATH):
     lib.wts_get_plan.restype = ctypes.c_int
     lib.wts_status_string.argtypes = [ctypes.c_int]
     lib.wts_status_string.restype = ctypes.c_char_p
+    lib.wts_check_log_ratio.argtypes = [c_int32, P(ctypes.c_int64)]
+    lib.wts_check_log_ratio.restype = ctypes.c_int
     return lib
 
 

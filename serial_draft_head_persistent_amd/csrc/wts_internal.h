@@ -136,6 +136,7 @@ hipError_t launch_walk(int wtype, int BB, const WalkArgs& a, int grid, int lds_b
 hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream_t s);
 hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
 hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s);
+hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);
 
 }  // namespace wts

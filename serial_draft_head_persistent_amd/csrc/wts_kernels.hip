@@ -85,6 +85,21 @@ constexpr float kLogC7 = (float)(1.0 / 7.0);
 constexpr float kLogC5 = (float)(1.0 / 5.0);
 constexpr float kLogC3 = (float)(1.0 / 3.0);
 
+// s = f / (2 + f) for the reduced argument of log_p (f = m - 1 with m in
+// [sqrt(1/2), sqrt(2))): a reciprocal estimate of the denominator, the
+// quotient, its exact residual (fused multiply-add) and one correction.  For
+// every f that log_p can produce this equals the correctly rounded binary32
+// quotient (all 2^23 reduced mantissas are compared with the IEEE division
+// on the device by check_log_ratio_kernel); it takes 4 instructions against
+// about 10 for the general division.
+__device__ __forceinline__ float log_ratio(float f) {
+  const float d = 2.0f + f;
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = f * r;
+  const float e = __builtin_fmaf(-q, d, f);
+  return __builtin_fmaf(e, r, q);
+}
+
 __device__ float log_p(float x) {
   const uint32_t bits = __float_as_uint(x);
   int e = (int)((bits >> 23) & 0xFFu) - 126;
@@ -94,7 +109,7 @@ __device__ float log_p(float x) {
     e = e - 1;
   }
   const float f = m - 1.0f;
-  const float s = f / (2.0f + f);
+  const float s = log_ratio(f);
   const float z = s * s;
   float p = kLogC9 * z;
   p = (p + kLogC7) * z;
@@ -1841,6 +1856,23 @@ hipError_t launch_step(int wtype, int BB, const WalkArgs& a, int grid, hipStream
 
 hipError_t launch_finish(const WalkArgs& a, hipStream_t s) {
   finish_kernel<<<1, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Every reduced log_p argument (one thread per mantissa): counts where
+// log_ratio differs from the IEEE quotient.
+__global__ __launch_bounds__(256) void check_log_ratio_kernel(unsigned long long* mismatches) {
+  const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (1u << 23)) return;
+  float m = __uint_as_float(k | 0x3F000000u);
+  if (m < 0.70710677f) m = m * 2.0f;
+  const float f = m - 1.0f;
+  const float ieee = f / (2.0f + f);
+  if (__float_as_uint(log_ratio(f)) != __float_as_uint(ieee)) atomicAdd(mismatches, 1ull);
+}
+
+hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s) {
+  check_log_ratio_kernel<<<(1u << 23) / 256, 256, 0, s>>>(mismatches);
   return hipGetLastError();
 }
 

@@ -352,6 +352,21 @@ wts_status wts_get_error(wts_ctx* ctx, int clear) {
   return (wts_status)err;
 }
 
+wts_status wts_check_log_ratio(int32_t device, int64_t* mismatches) {
+  if (!mismatches || device < 0) return WTS_ERR_INVALID_ARG;
+  DeviceGuard guard(device);
+  unsigned long long* d = nullptr;
+  if (hipMalloc((void**)&d, sizeof(*d)) != hipSuccess) return WTS_ERR_NO_MEMORY;
+  unsigned long long h = 0;
+  wts_status st = WTS_OK;
+  if (hipMemset(d, 0, sizeof(*d)) != hipSuccess || launch_check_log_ratio(d, nullptr) != hipSuccess ||
+      hipMemcpy(&h, d, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
+    st = WTS_ERR_DEVICE;
+  (void)hipFree(d);
+  *mismatches = (int64_t)h;
+  return st;
+}
+
 void wts_destroy(wts_ctx* ctx) {
   if (!ctx) return;
   DeviceGuard guard(ctx->device);

@@ -112,3 +112,13 @@ def test_watchdog_latches_timeout_and_grid_drains():
     h2, t2 = make_head(d, t)
     assert_exact(run(h2, t2), oracle_walk(d), "after time-out")
     h2.close()
+
+
+def test_log_ratio_shortcut_is_exact_everywhere():
+    # The noise kernels form the portable log's f / (2 + f) from a reciprocal
+    # estimate and one fused-multiply-add correction.  Over every argument that
+    # log can produce (all 2^23 reduced mantissas) it must equal the IEEE
+    # quotient bit for bit, or the T=1 walks could part from the oracle.
+    from serial_draft_head_persistent_amd import check_log_ratio
+    _print_case(test="log_ratio_exhaustive")
+    assert check_log_ratio(0) == 0
