@@ -159,6 +159,14 @@ __device__ float tanh_p(float x) {
   return x < 0.0f ? -r : r;
 }
 
+// Both halves of a 32x32->64 product from one instruction (v_mad_u64_u32)
+// rather than separate high and low multiplies.
+__device__ __forceinline__ void mul_wide(uint32_t m, uint32_t x, uint32_t& hi, uint32_t& lo) {
+  const uint64_t p = (uint64_t)m * (uint64_t)x;
+  hi = (uint32_t)(p >> 32);
+  lo = (uint32_t)p;
+}
+
 // Philox4x32-10 (Salmon et al., SC'11): 10 rounds of two 32x32->64 products,
 // Weyl key schedule between rounds.  Noise for (b, step, v): counter
 // (v >> 2, step, b, 0), key (seed_lo, seed_hi), output word v & 3.
@@ -170,8 +178,9 @@ __device__ float gumbel(uint32_t k0, uint32_t k1, int b, int step, int v) {
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    uint32_t hi0, lo0, hi1, lo1;
+    mul_wide(0xD2511F53u, c0, hi0, lo0);
+    mul_wide(0xCD9E8D57u, c2, hi1, lo1);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -1260,8 +1269,9 @@ __device__ __forceinline__ void make_noise(const WalkArgs& a, float* noise, int 
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
       }
-      const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-      const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+      uint32_t hi0, lo0, hi1, lo1;
+      mul_wide(0xD2511F53u, c0, hi0, lo0);
+      mul_wide(0xCD9E8D57u, c2, hi1, lo1);
       const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
       c0 = n0;
       c1 = lo1;
