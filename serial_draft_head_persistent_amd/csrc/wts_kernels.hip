@@ -574,14 +574,14 @@ struct LseAcc<NM, NE, false> {
 // With NZ, T=1 noise comes from LDS (computed one step ahead):
 // noise[b * a.noise_stride + (v - row0)], row0 = the workgroup's first row.
 // With LS, the logit also enters the running log-sum-exp pairs.
-template <int WT, int BB, int TEMP, bool NZ, bool LS>
+template <int WT, int BB, int TEMP, bool NZ, bool LS, bool GP = false>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                          const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
                                          float sw, const uint32_t (&bv)[Geo<WT, BB>::NE],
                                          const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                          typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                          LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
-                                         const float* noise, int row0) {
+                                         const float* noise, int row0, const float* gpre = nullptr) {
   using Gm = Geo<WT, BB>;
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
@@ -608,8 +608,10 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
       k = (ord16(lg) << 16) | lrow;
     } else {
       // lanes without a valid pair read the buffer's first element
-      const float g = NZ ? noise[okb ? b * a.noise_stride + (v - row0) : 0]
-                         : gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
+      // GP: this entry's noise was read from LDS at the start of the step
+      const float g = GP   ? gpre[e]
+                      : NZ ? noise[okb ? b * a.noise_stride + (v - row0) : 0]
+                           : gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
       const float sc = bf16_f32(lg) + g;
       k = ((unsigned long long)ord32(__float_as_uint(sc)) << 16) | lrow;
     }
@@ -1538,6 +1540,22 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
       for (int e = 0; e < Gm::NE; ++e) best[m][e] = 0;
     LseAcc<Gm::NM, Gm::NE, LS> ls;
     ls.init();
+    // T=1, three or four rows: the register groups' noise read from LDS now,
+    // so that the epilogues do not wait for it (measured slower at one row)
+    constexpr bool GP = NOISE && BB == 4;
+    float gzp[GP ? Gm::NG : 1][Gm::NM][Gm::NE];
+    if constexpr (GP) {
+#pragma unroll
+      for (int gi = 0; gi < Gm::NG; ++gi)
+#pragma unroll
+        for (int m = 0; m < Gm::NM; ++m)
+#pragma unroll
+          for (int e = 0; e < Gm::NE; ++e) {
+            const int b = ro.bent(m, e);
+            const bool okb = b < BB && gok(gi) && b < a.B;
+            gzp[gi][m][e] = noise[okb ? b * a.noise_stride + (gv(gi) - row0) : 0];
+          }
+    }
 
     // projection over the register-resident tiles, S tiles per accumulator
 #pragma unroll
@@ -1579,9 +1597,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
           }
           AT acc = pick_slot<Gm::S>(accs, ro.cslot);
           if (SPLIT) acc = acc + acc2;
-          epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
-                                            gok(gi), WT == 0 ? gsw[gi] : 0.0f, bnx[gi][m], shi, best, ls,
-                                            noise, row0);
+          epilogue<WT, BB, TEMP, NOISE, LS, GP>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
+                                                gok(gi), WT == 0 ? gsw[gi] : 0.0f, bnx[gi][m], shi, best, ls,
+                                                noise, row0, gzp[GP ? gi : 0][m]);
         }
       }
     }
