@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                          "of a --profile --copy-calib run into profiles/" + "walk_traffic.json and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print the per-dispatch mean of every counter in a rocprofv3 --pmc "
+                         "counter_collection.csv for the headline kernel, and exit")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --profile: also run a plain 512 MiB device copy (known bytes) so a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE")
@@ -79,6 +82,69 @@ def timed_walks(head, t, n, warmup, **kw):
     if err != "WTS_OK":
         raise RuntimeError(err)
     return total_ms / n, us
+
+
+def cold_walks(head, t, n, flush_bytes=512 << 20, **kw):
+    """Per-walk times (us) with the caches flushed before each walk: a write of
+    flush_bytes (twice the 256 MB memory-side cache) lands between walks, so
+    the entry's shard load and the base logits come from HBM."""
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=t["base"].device)
+    s = torch.cuda.current_stream()
+    out = head.walk(t["base"], t["x0"], h0=t.get("h0"), **kw)
+    us = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        out = head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+        b.record(s)
+        b.synchronize()
+        us.append(a.elapsed_time(b) * 1e3)
+    del scratch
+    err = head.error()
+    if err != "WTS_OK":
+        raise RuntimeError(err)
+    return np.array(us)
+
+
+CLOCK_GHZ = 2.4          # MI355X peak engine clock
+SIMDS_PER_CU = 4
+MFMA_CYCLES = 16         # v_mfma_i32_16x16x64_i8 and v_mfma_f32_16x16x32_bf16: 32,768 and
+                         # 16,384 ops per SIMD in 16 cycles, i.e. the published dense peaks
+
+
+def step_rooflines(plan, V, r, B, fit):
+    """Rooflines of the resident step and of the entry (int8 W, Markov, B rows).
+
+    Resident step: every W tile is an MFMA B operand read from registers or
+    LDS; the step cannot end before the busiest SIMD has issued the MFMAs of
+    its tiles (r/64 int8 MFMAs per tile, 16 cycles each).  At B=1 only the
+    hi/lo pair of rows in each MFMA's A block is distinct, so the useful int8
+    ops (2 vectors x 2 ops per MAC x V x r per batch row) are a small part of
+    the MFMA peak.  Entry: the shard's one-time load from HBM."""
+    tiles_cu = -(-plan["tiles"] // plan["grid"])
+    tiles_simd = -(-tiles_cu // SIMDS_PER_CU)
+    mfma_simd = tiles_simd * (r // 64)
+    bound_us = mfma_simd * MFMA_CYCLES / (CLOCK_GHZ * 1e3)
+    slope, entry = fit["per_step_us"], max(fit["entry_us"], 1e-3)
+    useful_ops = 2.0 * 2 * V * r * B
+    return {
+        "resident_step_roofline": {
+            "bound": "mfma issue, W operands on chip", "tiles_per_cu": tiles_cu,
+            "mfma_per_simd_per_step": mfma_simd, "bound_us": round(bound_us, 3),
+            "onchip_w_read_TBps_at_bound": round(V * r / (bound_us * 1e-6) / 1e12, 1),
+            "onchip_w_read_TBps": round(V * r / (slope * 1e-6) / 1e12, 1),
+            "frac": round(bound_us / slope, 4)},
+        "useful_int8_ops": {"ops_per_step": int(useful_ops),
+                            "achieved_TOPs": round(useful_ops / (slope * 1e-6) / 1e12, 1),
+                            "peak_TOPs": I8_PEAK_TOPS,
+                            "frac": round(useful_ops / (slope * 1e-6) / 1e12 / I8_PEAK_TOPS, 4)},
+        "entry_roofline": {"bound": "hbm", "bytes": int(V * r + 4 * V),
+                           "achieved_GBps": round((V * r + 4 * V) / (entry * 1e-6) / 1e9, 1),
+                           "peak_GBps": HBM_PEAK_GBS,
+                           "frac": round((V * r + 4 * V) / (entry * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
 
 
 def walk_stats(us):
@@ -144,6 +210,19 @@ def summarize_pmc(fetch_csv, write_csv):
     print(json.dumps(res))
 
 
+def summarize_counters(path):
+    """Per-dispatch means of the counters of one --pmc pass over the headline kernel."""
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if HEADLINE_KERNEL in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    res = {"kernel": HEADLINE_KERNEL, "source_sha256": kernel_source_hash(),
+           "dispatches": max((len(v) for v in vals.values()), default=0),
+           "per_dispatch_mean": {k: sum(v) / len(v) for k, v in sorted(vals.items())}}
+    print(json.dumps(res, indent=1))
+
+
 def committed_traffic():
     """Traffic of the headline kernel from the committed counter summary, or
     None if the kernel source changed since the counters were taken."""
@@ -203,6 +282,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
                           "(the walk's vocabulary sharding over several GPUs is a design note, not built)"}))
@@ -258,8 +340,12 @@ def main():
         "w_read_GBps_per_step": round(w_bytes / (fit["per_step_us"] * 1e-6) / 1e9, 1),
         "entry_w_load_GBps": round(w_bytes / (max(fit["entry_us"], 1e-3) * 1e-6) / 1e9, 1),
     }
+    per_step.update(step_rooflines(plan, V, r, B, fit))
+    log("per-step rooflines", per_step)
 
     extras = {"walk": walk_stats(us), "fit_resident": fit, "plan": plan}
+    extras["walk_cold_cache"] = walk_stats(cold_walks(head, t, 50))
+    log("cold-cache walks", extras["walk_cold_cache"])
     extras["breakdown_resident"] = breakdown(head, t)
     log("breakdown resident", extras["breakdown_resident"])
     extras["breakdown_stream"] = breakdown(head, t, exec="stream")

@@ -332,9 +332,15 @@ constexpr int kOffWin = kOffDone + 8;            // int [kMaxB]: staged row hold
 constexpr int kOffLseCnt = 1240;                 // int: waves done with this step's log-sum-exp pairs
 constexpr int kOffZero = 1280;                   // 256 zero bytes (A-operand source of other slots)
 constexpr int kOffCand = 1536;                   // u64 [kGroups][2]: group maxima seen so far
-constexpr int kOffRows = 2048;                   // [kGroups * 2][512]: staged candidate rows (hi | lo)
-constexpr int kRowBytes = 512;
-constexpr int kOffShs = kOffRows + kGroups * 2 * kRowBytes;  // float [kGroups * 2]: their s_hi
+// Staged candidate rows: hi at 0, lo at kLoOff of each row.  The 64-byte gap
+// puts the 16-byte chunks of the two halves that one A-operand read fetches
+// together (same k chunk, alternate A rows) in disjoint LDS banks.
+constexpr int kOffRows = 2048;                   // [kGroups][kRowBytes]
+constexpr int kLoOff = 320;
+constexpr int kRowBytes = kLoOff + 256;
+constexpr int kOffShs = kOffRows + kGroups * kRowBytes;  // float [kGroups]: their s_hi
+static_assert(kLoOff % 64 == 0 && kLoOff >= 256, "lo half past the hi half, on a 64-byte boundary");
+static_assert(kOffShs + 4 * kGroups <= lse_lds_offset(kHeadMarkov, 0, 1), "staged rows below the lse pairs");
 constexpr int kOffLat = 2048;                     // int8 [kMaxB][2][256] or bf16 [kMaxB][256]
 constexpr int kOffH = kOffLat + kMaxB * 512;       // float [kMaxB][256]
 constexpr int kOffAt = 32768;                      // recurrent: A bf16 as [k/8][256 j][8]
@@ -488,7 +494,7 @@ __device__ __forceinline__ void load_latent_staged(const WalkArgs& a, const Role
     const int b = ro.arow_b(m);
     const bool ok = b < a.B;
     const int slot = ok ? ((const int*)(lds + kOffWin))[b] : 0;
-    const char* src = lds + kOffRows + slot * kRowBytes + ro.arow_hl(m) * 256 + ro.q * 16;
+    const char* src = lds + kOffRows + slot * kRowBytes + ro.arow_hl(m) * kLoOff + ro.q * 16;
     const char* p = ok ? src : lds + kOffZero;
 #pragma unroll
     for (int c = 0; c < Gm::CH; ++c) lat[m][c] = *(const v4i*)(p + c * 64);
@@ -1118,8 +1124,11 @@ __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, 
     const int v = key_token(m & kKeyMask);
     if (v < 0 || v >= a.V) return;
     if (HEAD == kHeadMarkov) {
-      if (lane < 32)
-        __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + lane * 16),
+      // lane i fills bytes [16 i, 16 i + 16) of the staged row: lanes 0..15
+      // the hi half, lanes kLoOff/16.. the lo half
+      const int lo = lane - kLoOff / 16;
+      if (lane < 16 || (lo >= 0 && lo < 16))
+        __builtin_amdgcn_global_load_lds((const void*)(a.Eq + (size_t)v * 512 + (lane < 16 ? lane * 16 : 256 + lo * 16)),
                                          (lds_void*)(lds + kOffRows + bestc * kRowBytes), 16, 0, 0);
       if (lane == 0)
         __builtin_amdgcn_global_load_lds((const void*)(a.Es + v), (lds_void*)(lds + kOffShs + bestc * 4), 4, 0, 0);
@@ -1463,7 +1472,8 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
   if (HEAD == kHeadMarkov && CAND && fixed) {
     // the probe's latent, staged once where later steps read staged rows
-    if (tid < kRowBytes / 16) ((int4*)(lds + kOffRows))[tid] = ((const int4*)(a.Eq + (size_t)sx[0] * 512))[tid];
+    if (tid < 32)
+      ((int4*)(lds + kOffRows + (tid < 16 ? 0 : kLoOff - 256)))[tid] = ((const int4*)(a.Eq + (size_t)sx[0] * 512))[tid];
     if (tid == 0) {
       ((float*)(lds + kOffShs))[0] = a.Es[sx[0]];
       ((int*)(lds + kOffWin))[0] = 0;
