@@ -62,7 +62,7 @@ constexpr int lds_scratch_bytes(int head, int wtype, int BB) {
 // [result entries][64], at most 2 KiB; 1 KiB at B=1), in a part of the
 // scratch that nothing else of that kernel uses.
 constexpr int lse_lds_offset(int head, int wtype, int BB) {
-  return head == kHeadRecurrent ? (BB == 1 ? 29696 : 26624) : stage_candidates(head, wtype, BB) ? 18688 : 2048;
+  return head == kHeadRecurrent ? (BB == 1 ? 29696 : 27136) : stage_candidates(head, wtype, BB) ? 18688 : 2048;
 }
 
 constexpr int kMaxGrid = 256;   // workgroups of the persistent kernel at most

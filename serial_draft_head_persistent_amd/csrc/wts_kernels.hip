@@ -341,8 +341,16 @@ constexpr int kRowBytes = kLoOff + 256;
 constexpr int kOffShs = kOffRows + kGroups * kRowBytes;  // float [kGroups]: their s_hi
 static_assert(kLoOff % 64 == 0 && kLoOff >= 256, "lo half past the hi half, on a 64-byte boundary");
 static_assert(kOffShs + 4 * kGroups <= lse_lds_offset(kHeadMarkov, 0, 1), "staged rows below the lse pairs");
-constexpr int kOffLat = 2048;                     // int8 [kMaxB][2][256] or bf16 [kMaxB][256]
-constexpr int kOffH = kOffLat + kMaxB * 512;       // float [kMaxB][256]
+// Latent rows the recurrent head builds in LDS, 16 bytes longer than the
+// data, so that the distinct A rows one operand read fetches (hi and lo of
+// every batch row, same k chunk) start in different LDS banks.
+constexpr int kLatRow = 272;                       // int8 hi or lo row
+constexpr int kLatRowBF = 528;                     // bf16 row
+constexpr int kOffLat = 2048;                      // int8 [kMaxB][2][kLatRow] or bf16 [kMaxB][kLatRowBF]
+constexpr int kOffH = kOffLat + kMaxB * 2 * kLatRow;  // float [kMaxB][256]
+static_assert(kMaxB * kLatRowBF <= kMaxB * 2 * kLatRow, "bf16 rows fit the latent region");
+static_assert(kOffH + 4 * kR <= 12288, "one batch row's h below the staged E rows");
+static_assert(kOffH + 4 * kR * kMaxB <= lse_lds_offset(kHeadRecurrent, 0, 2), "h below the lse pairs");
 constexpr int kOffAt = 32768;                      // recurrent: A bf16 as [k/8][256 j][8]
 constexpr int kOffRecRows = 12288;                 // recurrent, one batch row: staged fp32 E rows [kGroups]
 constexpr int kRecRowBytes = kR * 4;
@@ -476,8 +484,8 @@ __device__ __forceinline__ void load_latent(const WalkArgs& a, const Roles<WT, B
 #pragma unroll
       for (int c = 0; c < Gm::CH; ++c) lat[m][c] = p[c * 4];
     } else {
-      const char* src = WT == 0 ? lds + kOffLat + (b * 2 + hl) * 256 + ro.q * 16
-                                : lds + kOffLat + (b * kR + ro.q * 8) * 2;
+      const char* src = WT == 0 ? lds + kOffLat + (b * 2 + hl) * kLatRow + ro.q * 16
+                                : lds + kOffLat + b * kLatRowBF + ro.q * 16;
 #pragma unroll
       for (int c = 0; c < Gm::CH; ++c) lat[m][c] = ok ? *(const v4i*)(src + c * 64) : v4i{0, 0, 0, 0};
     }
@@ -1194,11 +1202,11 @@ __device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, co
       const float u[4] = {u4.x, u4.y, u4.z, u4.w};
       uint32_t hi, lo;
       const float s = quant4(u, &hi, &lo);
-      *(uint32_t*)(lds + kOffLat + (b * 2 + 0) * 256 + lane * 4) = hi;
-      *(uint32_t*)(lds + kOffLat + (b * 2 + 1) * 256 + lane * 4) = lo;
+      *(uint32_t*)(lds + kOffLat + (b * 2 + 0) * kLatRow + lane * 4) = hi;
+      *(uint32_t*)(lds + kOffLat + (b * 2 + 1) * kLatRow + lane * 4) = lo;
       if (lane == 0) ((float*)(lds + kOffShi))[b] = s;
     } else {
-      uint16_t* lb = (uint16_t*)(lds + kOffLat) + b * kR + lane * 4;
+      uint16_t* lb = (uint16_t*)(lds + kOffLat + b * kLatRowBF) + lane * 4;
       lb[0] = (uint16_t)bf16_rne(u4.x);
       lb[1] = (uint16_t)bf16_rne(u4.y);
       lb[2] = (uint16_t)bf16_rne(u4.z);
