@@ -694,10 +694,11 @@ __device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB
   for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, d.bv[m]);
 }
 
-// Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), one tile of
-// prefetch.  `cur` holds tile i0 of this step, loaded before the step began
-// (a copy: its buffer is reused for the tiles after it).
-template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS, bool PP>
+// Tiles [i0, nw) of wave w, one tile per MFMA group (slot 0), D - 1 tiles of
+// prefetch (D buffers; D = 1: one buffer and a copy).  `cur` holds tile i0 of
+// this step, loaded before the step began (a copy: its buffer is reused for
+// the tiles after it).
+template <int WT, int BB, int TEMP, int NWV, bool NZ, bool LS, int D>
 __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int tb,
                                              int w, int i0, int nlds, int nw, const char* ldsw,
                                              TileBuf<WT, BB> cur,
@@ -726,7 +727,22 @@ __device__ __forceinline__ void stream_tiles(const WalkArgs& a, const Roles<WT, 
       epilogue<WT, BB, TEMP, NZ, LS>(a, ro, t, m, acc, v, lrow, ok, cur.sw, cur.bv[m], shi, best, ls, noise, row0);
     }
   };
-  if constexpr (PP) {
+  static_assert(D >= 1 && D <= 3, "one, two or three tile buffers");
+  if constexpr (D == 3) {
+    // Three buffers in turn, two tiles in flight while one is computed.
+    TileBuf<WT, BB> b1, b2;
+    if (i0 + 1 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i0 + 1, i0, nlds, ldsw, b1);
+    for (int i = i0; i < nw; i += 3) {
+      if (i + 2 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 2, i0, nlds, ldsw, b2);
+      compute(cur, i);
+      if (i + 1 >= nw) break;
+      if (i + 3 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 3, i0, nlds, ldsw, cur);
+      compute(b1, i + 1);
+      if (i + 2 >= nw) break;
+      if (i + 4 < nw) fetch_tile<WT, BB, NWV>(a, ro, t, tb, w, i + 4, i0, nlds, ldsw, b1);
+      compute(b2, i + 2);
+    }
+  } else if constexpr (D == 2) {
     // Two buffers used in turn: the next tile's loads go into the buffer that
     // is not being computed, and nothing is copied from a buffer whose loads
     // are still in flight (a copy would make the wave wait for them at once).
@@ -1648,9 +1664,12 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         }
       }
     } else if (nreg < nw) {
-      // two tile buffers unless the registers are short (T=1 at sixteen int8 rows, recurrent at T=1)
-      constexpr bool PP = !(TEMP == 1 && (HEAD == kHeadRecurrent || (WT == 0 && BB >= 16)));
-      stream_tiles<WT, BB, TEMP, NW, NOISE, LS, PP>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best,
+      // two tile buffers unless the registers are short (T=1 at sixteen int8 rows, recurrent at T=1);
+      // three for sixteen bf16 rows (one wave per SIMD; measured slower at eight rows)
+      constexpr int PD = TEMP == 1 && (HEAD == kHeadRecurrent || (WT == 0 && BB >= 16)) ? 1
+                         : NW == 4 && BB == 16 && !(LS && TEMP == 1)                      ? 3
+                                                                                          : 2;
+      stream_tiles<WT, BB, TEMP, NW, NOISE, LS, PD>(a, ro, t, tb, w, nreg, nlds, nw, ldsw, first, lat, shi, best,
                                                     ls, noise);
     }
     if (t + 1 < a.gamma) fetch_base(t + 1);
@@ -1775,7 +1794,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   if (nw > 0) {
     TileBuf<WT, BB> first;
     fetch_tile<WT, BB, kStepWaves>(a, ro, t, tb, w, 0, 0, 0, nullptr, first);
-    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS, true>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, lat, shi,
+    stream_tiles<WT, BB, TEMP, kStepWaves, false, LS, 2>(a, ro, t, tb, w, 0, 0, nw, nullptr, first, lat, shi,
                                                             best, ls, (const float*)nullptr);
   }
   reduce_to_lds<WT, BB, TEMP>(ro, w, best, red);
