@@ -214,3 +214,22 @@ def test_bf16_v248320_whole_shard_matches_streaming(B, T):
     assert_bf16_close(probe, oracle_walk(d, temperature=T, seed=3, keep_z=True, fixed_latent=True),
                       f"bf16 248k whole probe T={T}")
     h.close()
+
+
+@pytest.mark.parametrize("B,T", [(16, 0), (16, 1), (9, 0)])
+def test_bf16_v248320_sixteen_rows_resident_matches_streaming(B, T):
+    # sixteen-row bf16 walks stream two tiles ahead through three buffers; the
+    # partially resident walk (register, LDS, then streamed tiles) and the
+    # fully streamed one run the ring over different tile counts and must give
+    # identical bits (same fp32 order per tile)
+    d = cached_inputs(3, B=16, gamma=4)
+    _case(test="bf16_248k_ring", B=B, T=T)
+    h, t = make_head(d)
+    p = h.plan(B, temperature=T)
+    assert p["stream_tiles"] > 0 and p["reg_tiles"] > 0, p
+    ts = dict(t)
+    ts["base"], ts["x0"] = t["base"][:B].contiguous(), t["x0"][:B].contiguous()
+    got = run(h, ts, temperature=T, seed=4)
+    stream = run(h, ts, exec="stream", temperature=T, seed=4)
+    assert np.array_equal(got["tokens"], stream["tokens"]) and np.array_equal(got["logits"], stream["logits"])
+    h.close()
