@@ -13,6 +13,18 @@ def test_philox_known_answer_zero():
     assert [int(v) for v in out] == [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]
 
 
+def test_philox_known_answer_vectors():
+    # all published known-answer vectors (tests/golden/philox4x32_10_kat.txt)
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        w = [int(x, 16) for x in r]
+        out = philox4x32_10(np.array(w[:4], np.uint32), np.array(w[4:6], np.uint32))
+        assert [int(v) for v in out] == w[6:], r
+
+
 def test_philox_deterministic_and_key_sensitive():
     ctr = np.array([[7, 3, 1, 0], [8, 3, 1, 0]], np.uint32)
     a = philox4x32_10(ctr, np.array([1, 2], np.uint32))
