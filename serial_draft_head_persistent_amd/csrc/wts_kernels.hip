@@ -451,6 +451,15 @@ __device__ __forceinline__ unsigned long long row_max(unsigned long long x) {
 #undef WTS_DPP64
   return x;
 }
+// Max over each DPP row of a T=1 local key (32-bit score order << 16 | 16-bit
+// row field): the score order first, then the row field among the lanes that
+// hold that order.  Two 32-bit butterflies instead of one on 64 bits.
+__device__ __forceinline__ unsigned long long row_max_key48(unsigned long long x) {
+  const uint32_t hi = (uint32_t)(x >> 16);
+  const uint32_t mh = row_max(hi);
+  const uint32_t ml = row_max(hi == mh ? (uint32_t)(x & 0xFFFFu) : 0u);
+  return ((unsigned long long)mh << 16) | ml;
+}
 __device__ __forceinline__ uint32_t readlane(uint32_t x, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
 }
@@ -781,7 +790,9 @@ __device__ __forceinline__ void reduce_to_lds(const Roles<WT, BB>& ro, int w,
   for (int m = 0; m < Gm::NM; ++m)
 #pragma unroll
     for (int e = 0; e < Gm::NE; ++e) {
-      const K k = row_max(best[m][e]);
+      K k;
+      if constexpr (TEMP == 1) k = row_max_key48(best[m][e]);
+      else k = row_max(best[m][e]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cw0 = (4 * q) % Gm::RPS;
