@@ -368,10 +368,10 @@ def main():
                             "median_us_with": round(float(np.median(u1)), 2)}
         log("lse", extras["lse_t1"])
         # Fig. 12 analog: placement of the shard between registers and LDS
-        # (B=1, greedy); register tiles per wave r, the rest of the shard in LDS
+        # (B=1, greedy); nreg register tiles per wave, the rest of the shard in LDS
         place = []
-        for r in range(0, plan["reg_tiles"] + 1):
-            hp, _ = make_head(d, t, resident_tiles=r)
+        for nreg in range(0, plan["reg_tiles"] + 1):
+            hp, _ = make_head(d, t, resident_tiles=nreg)
             pp = hp.plan(1)
             fp = fit_steps(hp, d, t, n=50, warmup=5)
             place.append({"reg_tiles": pp["reg_tiles"], "lds_tiles": pp["lds_tiles"],
