@@ -60,3 +60,56 @@ def test_struct_layout_matches_c(cname, pyname):
     assert vals[0] == ctypes.sizeof(st)
     for f, off in zip(fields, vals[1:]):
         assert getattr(st, f).offset == off, f
+
+
+def _valid_create_params(_abi):
+    # fake, 256-byte aligned, never dereferenced: every case below is rejected
+    # before the library touches a device
+    fake = 0x7F0000000000
+    return _abi.CreateParams(V=4096, r=256, head=0, wtype=0, W=fake, w_scale=fake, E=fake, A=None, c=None,
+                             max_batch=16, max_steps=64, resident_tiles=-1, lds_tiles=-1, device=0,
+                             cooperative=0, watchdog_us=0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("V", 0, 1), ("V", 262144, 1), ("r", 0, 1), ("r", 128, 2), ("head", 2, 1), ("wtype", 2, 1),
+    ("W", None, 1), ("E", None, 1), ("w_scale", None, 1), ("max_batch", 0, 1), ("max_batch", 17, 1),
+    ("max_steps", 0, 1), ("max_steps", 65, 1), ("resident_tiles", -2, 1), ("lds_tiles", -2, 1),
+    ("W", 0x7F0000000008, 1), ("E", 0x7F0000000004, 1),
+])
+def test_create_rejects_bad_arguments_before_any_device_call(field, value, status):
+    """Host-detectable errors of wts_create return a status (1 = invalid
+    argument, 2 = unsupported) and leave *out NULL."""
+    from serial_draft_head_persistent_amd import _abi
+    lib = _abi.load()
+    p = _valid_create_params(_abi)
+    setattr(p, field, value)
+    h = ctypes.c_void_p(0x1234)
+    assert lib.wts_create(ctypes.byref(p), ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_recurrent_create_needs_A_and_c():
+    from serial_draft_head_persistent_amd import _abi
+    lib = _abi.load()
+    p = _valid_create_params(_abi)
+    p.head = 1
+    h = ctypes.c_void_p()
+    assert lib.wts_create(ctypes.byref(p), ctypes.byref(h)) == 1
+    p.A = 0x7F0000000000
+    assert lib.wts_create(ctypes.byref(p), ctypes.byref(h)) == 1  # c still missing
+    assert not h.value
+
+
+def test_null_context_and_params_are_rejected():
+    from serial_draft_head_persistent_amd import _abi
+    lib = _abi.load()
+    h = ctypes.c_void_p()
+    assert lib.wts_create(None, ctypes.byref(h)) == 1
+    p = _valid_create_params(_abi)
+    assert lib.wts_create(ctypes.byref(p), None) == 1
+    w = _abi.WalkParams(B=1, gamma=1)
+    assert lib.wts_walk(None, ctypes.byref(w)) == 1
+    plan = _abi.Plan()
+    assert lib.wts_get_plan(None, 1, 0, 0, ctypes.byref(plan)) == 1
+    lib.wts_destroy(None)  # a no-op
