@@ -392,7 +392,8 @@ def main():
                 tb = {"base": base, "x0": x0}
                 m, u = timed_walks(head, tb, 50, 5, temperature=T, seed=0)
                 sweep.append({"B": B_, "gamma": 16, "T": T, "median_us": round(float(np.median(u)), 2),
-                              "plan_reg_lds_stream": [head.plan(B_)[k] for k in ("reg_tiles", "lds_tiles", "stream_tiles")]})
+                              "plan_reg_lds_stream": [head.plan(B_, temperature=T)[k]
+                                                     for k in ("reg_tiles", "lds_tiles", "stream_tiles")]})
             log("sweep B", B_, sweep[-2:])
         extras["sweep_markov_int8_v151936"] = sweep
         head.close()

@@ -309,7 +309,7 @@ __global__ void bf16_rows_kernel(const float* __restrict__ E, long long n, uint1
 // rows per batch row (hi and lo for int8, one for bf16).  With RPS latent
 // rows per slot, S = 16 / RPS tiles share one A operand, each with its own
 // accumulator, and the lanes of result slot s take tile s.
-template <int WT, int BB, int HD = 0, bool FL = false>
+template <int WT, int BB, int HD = 0, bool FL = false, int TP = 0, bool LSP = false>
 struct Geo {
   static constexpr int LPB = WT == 0 ? 2 : 1;
   static constexpr int ROWS = LPB * BB;
@@ -317,7 +317,7 @@ struct Geo {
   static constexpr int RPS = ROWS <= 4 ? 4 : (ROWS <= 8 ? 8 : 16);
   static constexpr int S = 16 / RPS;
   static constexpr int CH = WT == 0 ? kChunksI8 : kChunksBF;
-  static constexpr int RT = FL ? reg_tiles_full(HD, WT, BB) : reg_tiles_max(HD, WT, BB);
+  static constexpr int RT = FL ? reg_tiles_full(HD, WT, BB) : reg_tiles_max(HD, WT, BB, TP, LSP);
   static constexpr int NG = (RT + S - 1) / S;
   static constexpr int NE = 4 / LPB;  // batch entries per lane and M block
 };
@@ -1399,7 +1399,7 @@ template <int WT, int BB, int HEAD, int TEMP, bool LS, bool FULL>
 __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkArgs a) {
   constexpr int NW = waves_for(HEAD, WT);
   constexpr int NT = NW * 64;
-  using Gm = Geo<WT, BB, HEAD, FULL>;
+  using Gm = Geo<WT, BB, HEAD, FULL, TEMP, LS>;
   using AT = typename AccT<WT>::T;
   constexpr int TB = WT == 0 ? kTileBytesI8 : kTileBytesBF;
   extern __shared__ __attribute__((aligned(16))) char lds[];

@@ -73,12 +73,12 @@ int wave_tiles(int cnt, int w, int NW) { return cnt > w ? (cnt - w + NW - 1) / N
 
 // Residency plan for one batch bucket.  *full: the whole shard fits on chip
 // in the variant with more register tiles and LDS tiles allotted per wave.
-void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, wts_plan* p, int* lds_bytes,
+void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, wts_plan* p, int* lds_bytes,
                int* noise_off = nullptr, int* noise_stride = nullptr, int* full = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
   const int NW = waves_for(ctx->head, ctx->wtype);
   const int per_wave = (per_wg + NW - 1) / NW;
-  int reg = std::min(reg_tiles_max(ctx->head, ctx->wtype, BB), per_wave);
+  int reg = std::min(reg_tiles_max(ctx->head, ctx->wtype, BB, temperature, lse), per_wave);
   if (ctx->reg_cap >= 0) reg = std::min(reg, ctx->reg_cap);
   const int tb = tile_bytes(ctx->wtype);
   const int stride = noise_floats(ctx, BB, temperature);
@@ -256,7 +256,7 @@ wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t tem
   if (exec < WTS_EXEC_RESIDENT || exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
   if (temperature != 0 && temperature != 1) return WTS_ERR_INVALID_ARG;
   int lds_bytes = 0;
-  make_plan(ctx, batch_bucket(B), exec, temperature, out, &lds_bytes);
+  make_plan(ctx, batch_bucket(B), exec, temperature, false, out, &lds_bytes);
   return WTS_OK;
 }
 
@@ -278,7 +278,8 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   wts_plan plan;
   int lds_bytes = 0;
   int noise_off = 0, noise_stride = 0, full = 0;
-  make_plan(ctx, BB, p->exec, p->temperature, &plan, &lds_bytes, &noise_off, &noise_stride, &full);
+  make_plan(ctx, BB, p->exec, p->temperature, p->lse_out != nullptr, &plan, &lds_bytes, &noise_off, &noise_stride,
+            &full);
 
   WalkArgs a{};
   a.Wp = ctx->Wp;
