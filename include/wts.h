@@ -162,7 +162,7 @@ wts_status wts_get_error(wts_ctx* ctx, int clear);
  * it asks for no lse_out (B selects the batch bucket 1, 2, 4, 8 or 16; larger
  * buckets keep fewer tiles in registers; T=1 Markov walks keep the next step's
  * noise in LDS, which can leave room for fewer LDS tiles).  An int8 Markov
- * walk of two to four rows that asks for lse_out, or runs at T=1, holds one
+ * walk of two to eight rows that asks for lse_out, or runs at T=1, holds one
  * register tile per wave fewer than a greedy one without it. */
 wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t temperature, wts_plan* out);
 
