@@ -163,8 +163,8 @@ wts_status wts_get_error(wts_ctx* ctx, int clear);
  * buckets keep fewer tiles in registers; T=1 Markov walks keep the next step's
  * noise in LDS, which can leave room for fewer LDS tiles).  A Markov walk
  * that asks for lse_out, or runs at T=1, holds one register tile per wave
- * fewer than a greedy one without it at two to eight int8 rows and at eight
- * or sixteen bf16 rows. */
+ * fewer than a greedy one without it at two to eight int8 rows and at four,
+ * eight or sixteen bf16 rows. */
 wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t temperature, wts_plan* out);
 
 /* Static description of a status code. */

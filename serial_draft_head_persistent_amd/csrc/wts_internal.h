@@ -23,13 +23,13 @@ constexpr int waves_for(int head, int wtype) { return (head == 0 && wtype == 1) 
 // in registers and more in LDS.  At two to eight int8 Markov rows the fifth
 // register tile fits only in greedy walks without the log normaliser (T=1
 // keys and noise, or the running log-sum-exp pairs, would spill); the same
-// holds for one extra bf16 tile at eight and sixteen rows.
+// holds for one extra bf16 tile at four, eight and sixteen rows.
 // The recurrent head also keeps its matrix-vector partial results across the
 // step, so it holds fewer.
 constexpr int reg_tiles_max(int head, int wtype, int BB, int temp, bool ls) {
   return wtype == 0 ? (head == 0 ? (BB == 1 ? 5 : BB <= 8 ? (temp == 0 && !ls ? 5 : 4) : 2)
                                  : (BB == 1 ? 5 : BB == 2 ? 4 : BB == 4 ? 3 : BB == 8 ? 2 : 1))
-                    : waves_for(head, wtype) == 4 ? (BB == 1 ? 9 : BB == 2 ? 8 : BB <= 4 ? 7 : BB == 8 ? (temp == 0 && !ls ? 7 : 6) : (temp == 0 && !ls ? 6 : 5)) : 1;
+                    : waves_for(head, wtype) == 4 ? (BB == 1 ? 9 : BB == 2 ? 8 : BB <= 4 ? (temp == 0 && !ls ? 8 : 7) : BB == 8 ? (temp == 0 && !ls ? 7 : 6) : (temp == 0 && !ls ? 6 : 5)) : 1;
 }
 // Register tiles per wave of the whole-shard-on-chip variant (bf16 Markov
 // walks of up to four batch rows): without streaming buffers a wave can hold
