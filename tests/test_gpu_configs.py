@@ -233,3 +233,22 @@ def test_bf16_v248320_sixteen_rows_resident_matches_streaming(B, T):
     stream = run(h, ts, exec="stream", temperature=T, seed=4)
     assert np.array_equal(got["tokens"], stream["tokens"]) and np.array_equal(got["logits"], stream["logits"])
     h.close()
+
+
+@pytest.mark.parametrize("B", [2, 4, 8])
+def test_greedy_split_with_and_without_lse_full_size(head152, B):
+    # Greedy walks of two to eight int8 rows hold five register tiles per wave;
+    # with the log normaliser (or at T=1) four plus one LDS tile.  The two
+    # splits run different kernels over the same shard and must give the same
+    # bits.
+    from gpu_helpers import assert_lse_close
+    d, h, t = head152
+    _case(test="lse_split_full", B=B)
+    p0, p1 = h.plan(B, temperature=0), h.plan(B, temperature=1)
+    assert (p0["reg_tiles"], p0["lds_tiles"]) == (5, 0) and (p1["reg_tiles"], p1["lds_tiles"]) == (4, 1), (p0, p1)
+    ds, ts = _slice(d, t, B, 16)
+    plain = run(h, ts)
+    with_lse = run(h, ts, lse=True)
+    assert np.array_equal(plain["tokens"], with_lse["tokens"])
+    assert np.array_equal(plain["logits"], with_lse["logits"])
+    assert_lse_close(with_lse["lse"], with_lse["logits"], f"lse split B={B}")
