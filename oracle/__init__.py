@@ -23,5 +23,5 @@ from .quant import quant_hilo  # noqa: F401
 from .philox import philox4x32_10, uniform24, gumbel_noise  # noqa: F401
 from .walk import (  # noqa: F401
     order_key, select_token, project_int8, epilogue_int8, project_bf16,
-    fma32, recurrent_update, log_normaliser, walk,
+    recurrent_preact, recurrent_update, log_normaliser, walk,
 )

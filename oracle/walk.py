@@ -25,11 +25,11 @@ the design notes):
   * selection is on the returned bf16 logit widened to binary32 (T=0), or on
     fp32(logit + g) with the Gumbel noise g of ``oracle.philox`` (T=1);
     the largest score wins, ties go to the lowest index, -0 equals +0.
-  * recurrent pre-activation: the sum acc_j = sum_k A[j,k] h[k] is taken in
-    binary32 as eight partial sums s_i over k = i, i+8, i+16, ... (each in
-    ascending k, each term one fused multiply-add: s_i = RN(A[j,k] h[k] + s_i)),
-    combined as ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)); pre = (acc_j + E[x][j]) +
-    c[j], h_j = tanh_p(pre).
+  * recurrent pre-activation: the pages give h = tanh(A h + E[x] + c) and no
+    summation order, so the plainest one is taken: acc_j = sum_k A[j,k] h[k]
+    as one chain in ascending k starting from +0, each term multiplied and
+    then added with one binary32 rounding per operation (no fused
+    multiply-add); pre = (acc_j + E[x][j]) + c[j]; h_j = tanh_p(pre).
   * fixed-latent probe (Fig. 13b): every step projects and selects with the
     latent of step 0 (Markov: E[x_0]; recurrent: h_1); the chosen tokens are
     emitted but do not feed back.
@@ -106,42 +106,26 @@ def project_bf16(Wb_f64, u_bits):
     return (Wb_f64 @ u).astype(np.float32)
 
 
-def fma32(a, b, c):
-    """Fused multiply-add in binary32, RN(a b + c) with one rounding (IEEE-754 fma).
+def recurrent_preact(A_f32, h, e_row, c):
+    """Pre-activation of the recurrent state, ((sum_k A[:,k] h[k]) + e_row) + c.
 
-    a must hold bf16 values (at most 8 significant bits) and b binary32
-    values, so a b (at most 32 significant bits) is exact in binary64.  The
-    sum is formed in binary64 rounded to odd -- the exact error of the
-    binary64 sum (TwoSum, Knuth) tells whether it was inexact -- and a value
-    rounded to odd with 53 bits rounds to the same binary32 number as the exact
-    sum.
+    Weights That Stay, Fig. 13 (recurrent heads): the state update is
+    h = tanh(A h + E[x] + c); no summation order is given, so the sum is one
+    binary32 chain in ascending k from +0: acc = RN(acc + RN(A[j,k] h[k])),
+    a separate rounding for every product and every addition.  A_f32 holds
+    the bf16 matrix widened exactly to binary32 ([r, r], row j = output j).
     """
-    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
-    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
-    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
-    p = a64 * b64
-    s = p + c64
-    bb = s - p
-    err = (p - (s - bb)) + (c64 - bb)
-    odd = (s.view(np.int64) & 1) == 1
-    s = np.where((err != 0) & ~odd, np.nextafter(s, np.where(err > 0, np.inf, -np.inf)), s)
-    return s.astype(np.float32)
+    acc = np.zeros(A_f32.shape[0], dtype=np.float32)
+    for k in range(h.shape[-1]):
+        prod = A_f32[:, k] * np.float32(h[k])      # binary32 product, rounded once
+        acc = acc + prod                            # binary32 sum, rounded once
+    pre = acc + np.asarray(e_row, dtype=np.float32)
+    return pre + np.asarray(c, dtype=np.float32)
 
 
 def recurrent_update(A_f32, h, e_row, c):
-    """h_new = tanh_p((sum_k A[:,k] h[k]) + e_row + c).
-
-    The binary32 sum runs as eight interleaved partial sums (k mod 8, each
-    ascending, one fused multiply-add per term) combined in a fixed pairwise
-    tree.
-    """
-    r = h.shape[-1]
-    s = [np.zeros(A_f32.shape[0], dtype=np.float32) for _ in range(8)]
-    for k in range(r):
-        s[k % 8] = fma32(A_f32[:, k], np.float32(h[k]), s[k % 8])
-    acc = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]))
-    pre = (acc + np.asarray(e_row, dtype=np.float32)) + np.asarray(c, dtype=np.float32)
-    return tanh_p(pre)
+    """h_new = tanh_p(recurrent_preact(A_f32, h, e_row, c)) (Fig. 13)."""
+    return tanh_p(recurrent_preact(A_f32, h, e_row, c))
 
 
 def log_normaliser(logit_bits):

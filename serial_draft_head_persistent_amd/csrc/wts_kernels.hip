@@ -32,8 +32,7 @@
 //    ~11 us per step), and the all-gather needs none.
 //
 // Bit-exactness with the host reference needs: no contraction of a*b+c
-// (built with -ffp-contract=off; the recurrent sum's fused multiply-adds are
-// explicit fmaf calls), IEEE division (default), rintf half-even.
+// (built with -ffp-contract=off), IEEE division (default), rintf half-even.
 
 #include "wts_internal.h"
 
@@ -1202,7 +1201,7 @@ __device__ __forceinline__ void stage_rows(const WalkArgs& a, int t, char* lds, 
 }
 
 // Recurrent head, first half of a step (Fig. 13): h_{t+1} = tanh(A h_t +
-// E[x_t] + c) with the A h_t sums (ascending k) already in acc; then the
+// E[x_t] + c) with the A h_t sums (ascending k) already in racc; then the
 // latent rows for the projection (int8 hi/lo + s_hi, or bf16) into LDS.
 // staged: E[x_t] is the candidate row staged in LDS during the exchange.
 template <int WT, int BB>
@@ -1243,11 +1242,14 @@ __device__ __forceinline__ void recurrent_advance(const WalkArgs& a, int tid, co
   __syncthreads();
 }
 
-// Recurrent head: racc[b] = sum_k A[j][k] h[b][k] in binary32 as eight
-// interleaved partial sums (k mod 8, ascending k in each, one fused
-// multiply-add per term) combined as ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)):
-// eight independent chains per thread.  A lives in LDS as [k/8][j][8] bf16, so thread j reads the eight
-// weights of a k-block with one 16-byte load; h is read as a broadcast.
+// Recurrent head (Fig. 13 gives h = tanh(A h + E[x] + c), no summation
+// order): racc[b] = sum_k A[j][k] h[b][k] in binary32 as one chain in
+// ascending k from +0, every product and every addition rounded once (no
+// fused multiply-add; the build disables contraction).  Thread j owns output
+// j.  A lives in LDS as [k/8][j][8] bf16, so thread j reads the eight
+// weights of a k-block with one 16-byte load, widened once and used for every
+// batch row; h is read as a broadcast.  The chains of the batch rows are
+// independent and interleave.
 template <int BB>
 __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, const char* lds, float (&racc)[BB]) {
   if (tid < kThreads - kR) return;
@@ -1255,43 +1257,39 @@ __device__ __forceinline__ void recurrent_matvec(const WalkArgs& a, int tid, con
   const uint4* A8 = (const uint4*)(lds + kOffAt);
   const float* h = (const float*)(lds + kOffH);
 #pragma unroll
-  for (int b = 0; b < BB; ++b) {
-    if (b >= a.B) {
-      racc[b] = 0.0f;
-      continue;
-    }
-    float ps[8];
+  for (int b = 0; b < BB; ++b) racc[b] = 0.0f;
+  // A loads run D k-blocks ahead of the arithmetic
+  constexpr int KB = kR / 8, D = 2;
+  uint4 wq[D + 1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ps[i] = 0.0f;
-    // LDS loads run two k-blocks ahead of the arithmetic
-    constexpr int KB = kR / 8, D = BB >= 16 ? 1 : 2;
-    uint4 wq[D + 1];
-    float4 hq0[D + 1], hq1[D + 1];
+  for (int d = 0; d < D; ++d) wq[d] = A8[d * kR + j];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      wq[d] = A8[d * kR + j];
-      hq0[d] = *(const float4*)(h + b * kR + d * 8);
-      hq1[d] = *(const float4*)(h + b * kR + d * 8 + 4);
-    }
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kb + D < KB) wq[(kb + D) % (D + 1)] = A8[(kb + D) * kR + j];
+    const uint4 w8 = wq[kb % (D + 1)];
+    float av[8];
+    av[0] = __uint_as_float(w8.x << 16);
+    av[1] = __uint_as_float(w8.x & 0xFFFF0000u);
+    av[2] = __uint_as_float(w8.y << 16);
+    av[3] = __uint_as_float(w8.y & 0xFFFF0000u);
+    av[4] = __uint_as_float(w8.z << 16);
+    av[5] = __uint_as_float(w8.z & 0xFFFF0000u);
+    av[6] = __uint_as_float(w8.w << 16);
+    av[7] = __uint_as_float(w8.w & 0xFFFF0000u);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (kb + D < KB) {
-        wq[(kb + D) % (D + 1)] = A8[(kb + D) * kR + j];
-        hq0[(kb + D) % (D + 1)] = *(const float4*)(h + b * kR + (kb + D) * 8);
-        hq1[(kb + D) % (D + 1)] = *(const float4*)(h + b * kR + (kb + D) * 8 + 4);
+    for (int b = 0; b < BB; ++b) {
+      if (b >= a.B) continue;
+      const float4 h0 = *(const float4*)(h + b * kR + kb * 8);
+      const float4 h1 = *(const float4*)(h + b * kR + kb * 8 + 4);
+      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      float acc = racc[b];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = av[i] * hv[i];
+        acc = acc + p;
       }
-      const uint4 w8 = wq[kb % (D + 1)];
-      const float4 h0 = hq0[kb % (D + 1)], h1 = hq1[kb % (D + 1)];
-      ps[0] = fmaf(__uint_as_float(w8.x << 16), h0.x, ps[0]);
-      ps[1] = fmaf(__uint_as_float(w8.x & 0xFFFF0000u), h0.y, ps[1]);
-      ps[2] = fmaf(__uint_as_float(w8.y << 16), h0.z, ps[2]);
-      ps[3] = fmaf(__uint_as_float(w8.y & 0xFFFF0000u), h0.w, ps[3]);
-      ps[4] = fmaf(__uint_as_float(w8.z << 16), h1.x, ps[4]);
-      ps[5] = fmaf(__uint_as_float(w8.z & 0xFFFF0000u), h1.y, ps[5]);
-      ps[6] = fmaf(__uint_as_float(w8.w << 16), h1.z, ps[6]);
-      ps[7] = fmaf(__uint_as_float(w8.w & 0xFFFF0000u), h1.w, ps[7]);
+      racc[b] = acc;
     }
-    racc[b] = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
   }
 }
 

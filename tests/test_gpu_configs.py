@@ -111,7 +111,7 @@ def test_config3_bf16_tolerance(B):
     ts["base"], ts["x0"] = t["base"][:B].contiguous(), t["x0"][:B].contiguous()
     got = run(h, ts)
     ref = oracle_walk(ds, keep_z=True)
-    acc = assert_bf16_close(got, ref, f"bf16 B={B}")
+    acc = assert_bf16_close(got, ref, f"bf16 B={B}", d=ds)
     print("accepted near-tie token mismatches:", acc, flush=True)
     h.close()
 
@@ -122,7 +122,7 @@ def test_bf16_small_tolerance_all_modes():
     h, t = make_head(d)
     ref = oracle_walk(d, keep_z=True)
     res = run(h, t)
-    assert_bf16_close(res, ref, "bf16 small")
+    assert_bf16_close(res, ref, "bf16 small", d=d)
     for ex in ("stream", "stepwise"):
         got = run(h, t, exec=ex)
         # fp32 accumulation order is fixed per tile, so all modes agree bitwise
@@ -178,7 +178,7 @@ def test_bf16_v151936_fully_resident(B):
     p = h.plan(B)
     assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 151936 * 512, p
     got = run(h, t)
-    assert_bf16_close(got, oracle_walk(d, keep_z=True), f"bf16 152k B={B}")
+    assert_bf16_close(got, oracle_walk(d, keep_z=True), f"bf16 152k B={B}", d=d)
     stream = run(h, t, exec="stream")
     assert np.array_equal(stream["logits"], got["logits"]) and np.array_equal(stream["tokens"], got["tokens"])
     h.close()
@@ -209,10 +209,11 @@ def test_bf16_v248320_whole_shard_matches_streaming(B, T):
     stream = run(h, t, exec="stream", temperature=T, seed=3, lse=True)
     assert np.array_equal(got["tokens"], stream["tokens"]) and np.array_equal(got["logits"], stream["logits"])
     assert np.allclose(got["lse"], stream["lse"], rtol=1e-5, atol=0)
-    assert_bf16_close(got, oracle_walk(d, temperature=T, seed=3, keep_z=True), f"bf16 248k whole B={B} T={T}")
+    assert_bf16_close(got, oracle_walk(d, temperature=T, seed=3, keep_z=True), f"bf16 248k whole B={B} T={T}",
+                      d=d, temperature=T, seed=3)
     probe = run(h, t, temperature=T, seed=3, fixed_latent=True)
     assert_bf16_close(probe, oracle_walk(d, temperature=T, seed=3, keep_z=True, fixed_latent=True),
-                      f"bf16 248k whole probe T={T}")
+                      f"bf16 248k whole probe T={T}", d=d, temperature=T, seed=3, fixed_latent=True)
     h.close()
 
 

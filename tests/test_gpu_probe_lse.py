@@ -66,7 +66,8 @@ def test_fixed_latent_bf16_close(exec_):
     _print_case(test="fixed_latent_bf16", V=5000, B=2, exec=exec_)
     h, t = make_head(d)
     got = run(h, t, exec=exec_, fixed_latent=True)
-    assert_bf16_close(got, oracle_walk(d, keep_z=True, fixed_latent=True), f"probe bf16 {exec_}")
+    assert_bf16_close(got, oracle_walk(d, keep_z=True, fixed_latent=True), f"probe bf16 {exec_}", d=d,
+                      fixed_latent=True)
     h.close()
 
 
@@ -105,7 +106,8 @@ def test_lse_bf16(B):
     _print_case(test="lse_bf16", V=6007, B=B)
     h, t = make_head(d)
     got = run(h, t, temperature=1, seed=5, lse=True)
-    assert_bf16_close(got, oracle_walk(d, temperature=1, seed=5, keep_z=True), f"lse bf16 B={B}")
+    assert_bf16_close(got, oracle_walk(d, temperature=1, seed=5, keep_z=True), f"lse bf16 B={B}", d=d,
+                      temperature=1, seed=5)
     assert_lse_close(got["lse"], got["logits"], f"lse bf16 B={B}")
     h.close()
 

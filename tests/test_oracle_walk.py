@@ -52,11 +52,9 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0, fixed=False):
                 A = bf16_to_f32(d["A"])
                 hn = []
                 for j in range(r):
-                    ps = [Fraction(0)] * 8   # eight interleaved partial sums, fixed tree
-                    for k in range(r):       # one fused multiply-add per term
-                        ps[k % 8] = rnd32(ps[k % 8] + _F(A[j, k]) * _F(h[k]))
-                    acc = rnd32(rnd32(rnd32(ps[0] + ps[1]) + rnd32(ps[2] + ps[3]))
-                                + rnd32(rnd32(ps[4] + ps[5]) + rnd32(ps[6] + ps[7])))
+                    acc = Fraction(0)         # one chain in ascending k, product and sum rounded apart
+                    for k in range(r):
+                        acc = rnd32(acc + rnd32(_F(A[j, k]) * _F(h[k])))
                     pre = rnd32(rnd32(acc + _F(E[x, j])) + _F(d["c"][j]))
                     hn.append(tanh_p(np.float32(float(pre))))
                 h = hn
@@ -85,9 +83,7 @@ def _brute_walk(d, temperature=0, seed=0, step_offset=0, fixed=False):
 @pytest.mark.parametrize("head", ["markov", "recurrent"])
 def test_toy_walk_brute_force(temperature, head):
     # Fig. 2 toy shape: V=12, r=4, three steps (two batch rows)
-    # recurrent: r=16 so that every one of the eight partial sums has two terms
-    r = 4 if head == "markov" else 16
-    d = datagen.make_inputs(12, r, 2, 3, head=head, seed=11)
+    d = datagen.make_inputs(12, 4, 2, 3, head=head, seed=11)
     toks, lg = _brute_walk(d, temperature, seed=3)
     o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head=head,
                     A=d["A"], c=d["c"], h0=d["h0"], temperature=temperature, seed=3)
@@ -214,15 +210,30 @@ def test_resume_invariance(head):
 
 
 def test_batch_rows_independent():
+    # Rows of a batch share only W and E (and A, c): at T=0 row b of a batched
+    # walk is the walk of row b alone.  At T=1 the noise is keyed by the batch
+    # index, so batch row 0 equals a lone walk, and row b equals a lone walk
+    # that draws row b's noise -- checked through the Gumbel-max rule itself:
+    # each chosen token is the argmax of fp32(logit + g(seed, b, t, v)).
     d = datagen.make_inputs(400, 32, 3, 5, seed=17)
-    full = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], temperature=1, seed=5)
+    greedy = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"])
+    hot = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], temperature=1, seed=5)
     for b in range(3):
         one = oracle.walk(d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"])
-        g = oracle.walk(d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"])
-        assert np.array_equal(one["tokens"], g["tokens"])
-    # T=1 noise is keyed by the batch index, so row b of a batch differs from a lone row 0
-    lone = oracle.walk(d["W"], d["E"], d["base"][2:3], d["x0"][2:3], s_w=d["s_w"], temperature=1, seed=5)
-    assert lone["tokens"].shape == (1, 5) and full["tokens"].shape == (3, 5)
+        assert np.array_equal(greedy["tokens"][b:b + 1], one["tokens"])
+        assert np.array_equal(greedy["logits"][b:b + 1], one["logits"])
+        lone = oracle.walk(d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"],
+                           temperature=1, seed=5)
+        if b == 0:
+            assert np.array_equal(hot["tokens"][:1], lone["tokens"])
+        for t in range(5):
+            g = oracle.gumbel_noise(5, b, t, np.arange(400))
+            sc = (bf16_to_f32(hot["logits"][b, t]) + g).astype(np.float32)
+            assert hot["tokens"][b, t] == int(np.argmax(sc))
+    # the T=1 walks of rows 1 and 2 take other noise than a lone row would
+    assert not all(np.array_equal(hot["tokens"][b], oracle.walk(
+        d["W"], d["E"], d["base"][b:b + 1], d["x0"][b:b + 1], s_w=d["s_w"], temperature=1,
+        seed=5)["tokens"][0]) for b in (1, 2))
 
 
 def test_project_bf16_exact_sum():
@@ -256,8 +267,7 @@ def test_bf16_walk_bruteforce_small():
 @pytest.mark.parametrize("head", ["markov", "recurrent"])
 def test_fixed_latent_brute_force(temperature, head):
     # the probe of Fig. 13b on the toy shape: every op with exact rationals
-    r = 4 if head == "markov" else 16
-    d = datagen.make_inputs(12, r, 2, 4, head=head, seed=21)
+    d = datagen.make_inputs(12, 4, 2, 4, head=head, seed=21)
     toks, lg = _brute_walk(d, temperature, seed=4, fixed=True)
     o = oracle.walk(d["W"], d["E"], d["base"], d["x0"], s_w=d["s_w"], head=head, A=d["A"],
                     c=d["c"], h0=d["h0"], temperature=temperature, seed=4, fixed_latent=True)
@@ -338,24 +348,71 @@ def test_walk_lse_is_normaliser_of_its_logits():
             assert o["lse"][b, t] == log_normaliser(o["logits"][b, t])
 
 
-def test_fma32_exact_against_rationals():
-    # RN32(a b + c) with a bf16-valued, b and c binary32: against exact rationals,
-    # including sums that cancel almost completely and exact ties
-    rng = np.random.default_rng(27)
-    n = 20000
-    a = bf16_to_f32(bf16_rne(rng.normal(0, 1, n).astype(np.float32)))
-    b = rng.normal(0, 1, n).astype(np.float32)
-    c = rng.normal(0, 1, n).astype(np.float32)
-    c[: n // 4] = (-(a[: n // 4].astype(np.float64) * b[: n // 4]).astype(np.float32))  # near cancellation
-    c[n // 4: n // 2] *= np.float32(2.0 ** -30)                                          # tiny addend
-    got = oracle.fma32(a, b, c)
-    for i in range(0, n, 7):
-        want = rnd32(_F(a[i]) * _F(b[i]) + _F(c[i]))
-        assert Fraction(float(got[i])) == want, (a[i], b[i], c[i])
-    # ties: a b + c exactly halfway between two binary32 values
-    one = np.float32(1.0)
-    half_ulp = np.float32(2.0 ** -24)
-    got = oracle.fma32(np.array([one, one], np.float32), np.array([one, np.float32(1.0 + 2.0 ** -23)], np.float32),
-                       np.array([half_ulp, half_ulp], np.float32))
-    assert got[0] == np.float32(1.0)                      # 1 + 2^-24 ties to even (1)
-    assert got[1] == np.float32(1.0 + 2.0 ** -22)         # 1 + 2^-23 + 2^-24 ties to even (up)
+# ---- the recurrent sum order (pins by hand-derived IEEE results) ----
+# The pages give h = tanh(A h + E[x] + c) with no summation order (Fig. 13);
+# the oracle takes one ascending chain with a rounding after every product
+# and every addition, then (acc + E[x]) + c.  Each case below has a result
+# worked out by hand from the binary32 rounding rule, and a summation in
+# any other grouping, with fused multiply-adds, or in higher precision gives
+# a different number.
+
+def _preact(A_rows, h, e=0.0, c=0.0):
+    A = np.asarray(A_rows, np.float32)
+    n = A.shape[1]
+    return oracle.recurrent_preact(A, np.asarray(h, np.float32), np.full(A.shape[0], e, np.float32),
+                                   np.full(A.shape[0], c, np.float32))
+
+
+def test_recurrent_sum_is_ascending_chain():
+    # 1 followed by 255 terms of 2^-24 (half an ulp of 1): each addition to 1
+    # is an exact tie and rounds to the even neighbour, 1, so the ascending
+    # chain ends at exactly 1.  Summed in any order that adds small terms
+    # together first (reversed, pairwise, interleaved partial sums) or exactly
+    # and rounded once, the result is 1 + 2^-16 (127.5 ulps of 1, a tie that
+    # rounds to the even 128).
+    h = np.full(256, 2.0 ** -24, np.float32)
+    h[0] = 1.0
+    A = np.ones((1, 256), np.float32)
+    assert _preact(A, h)[0] == np.float32(1.0)
+    # reversed rows: the tiny terms first, then 1 at the end
+    assert _preact(A[:, ::-1], h[::-1])[0] == np.float32(1.0 + 2.0 ** -16)
+    # the terms before k = 0 matter the same way: 2^-24 terms then 1 (ascending chain
+    # sums them exactly to 255 * 2^-24 first)
+    h2 = np.full(256, 2.0 ** -24, np.float32)
+    h2[255] = 1.0
+    assert _preact(A, h2)[0] == np.float32(1.0 + 2.0 ** -16)
+
+
+def test_recurrent_products_rounded_before_the_sum():
+    # A[0] = -1, h[0] = 1 + 2^-7 + 2^-23 (exact in binary32), then
+    # A[1] = 1 + 2^-7 (exact in bf16), h[1] = 1 + 2^-23: the exact product is
+    # 1 + 2^-7 + 2^-23 + 2^-30, which rounds to 1 + 2^-7 + 2^-23 (the 2^-30
+    # bit is below half an ulp), so the chain ends at exactly +0.  A fused
+    # multiply-add would keep the 2^-30.
+    h = np.zeros(256, np.float32)
+    A = np.zeros((1, 256), np.float32)
+    A[0, 0], h[0] = -1.0, np.float32(1.0 + 2.0 ** -7 + 2.0 ** -23)
+    A[0, 1], h[1] = np.float32(1.0 + 2.0 ** -7), np.float32(1.0 + 2.0 ** -23)
+    assert float(A[0, 1]) == float(bf16_to_f32(bf16_rne(A[0, 1])))
+    got = _preact(A, h)[0]
+    assert got == np.float32(0.0) and not np.signbit(got)
+
+
+def test_recurrent_pre_adds_embedding_then_bias():
+    # acc = 1 (A = e_0, h_0 = 1), E[x] = c = 2^-24: (1 + 2^-24) ties to 1,
+    # then + 2^-24 ties to 1 again; adding E[x] + c first would give
+    # 1 + 2^-23.
+    h = np.zeros(256, np.float32)
+    h[0] = 1.0
+    A = np.zeros((1, 256), np.float32)
+    A[0, 0] = 1.0
+    assert _preact(A, h, e=2.0 ** -24, c=2.0 ** -24)[0] == np.float32(1.0)
+    # and with E[x] = -1, c = 2^-24: (1 - 1) + 2^-24 = 2^-24 exactly
+    assert _preact(A, h, e=-1.0, c=2.0 ** -24)[0] == np.float32(2.0 ** -24)
+
+
+def test_recurrent_chain_starts_from_positive_zero():
+    # all products -0 (A = -1, h = +0): +0 + (-0) = +0 in round-to-nearest
+    A = -np.ones((3, 256), np.float32)
+    got = _preact(A, np.zeros(256, np.float32))
+    assert np.all(got == 0) and not np.any(np.signbit(got))
