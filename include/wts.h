@@ -150,6 +150,27 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out);
  * [b][t] = token chosen at step t, and optionally logits_out and state_out. */
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * walk as wts_walk, with the same arguments, outputs and bits, but the
+ * scratch its kernels use -- the control block of the cross-workgroup
+ * exchange and the step-wise slots, the error word, and the per-workgroup
+ * log-normaliser partials -- lives in a fixed array of the library on each
+ * GPU (set up and cleared by the first wts_create on that GPU, held until the
+ * process ends) instead of in the context.  Allocates nothing and calls no
+ * allocating routine.  Limit: the partials of one walk that asks for lse_out
+ * must fit in WTS_NOALLOC_LSE_BYTES (8 bytes per batch row, step and
+ * workgroup; B * gamma * 256 * 8 for persistent walks on 256 compute units,
+ * B * gamma * ceil(V/128) * 8 for step-wise walks); beyond it the call
+ * returns WTS_ERR_UNSUPPORTED before anything is enqueued.  Every context on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (from any
+ * context) race and must not be issued; the array keeps the last walk's
+ * contents, and each walk clears what the next one needs at zero.  Device
+ * errors of these walks are reported by wts_get_error on any context of that
+ * GPU. */
+#define WTS_NOALLOC_LSE_BYTES (1 << 20)
+wts_status wts_walk_noalloc(wts_ctx* ctx, const wts_walk_params* p);
+
 /* Synchronizes the device, then frees everything the context owns.
  * NULL is ignored. */
 void wts_destroy(wts_ctx* ctx);

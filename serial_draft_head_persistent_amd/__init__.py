@@ -68,7 +68,7 @@ class Head:
 
     def walk(self, base, x0, *, h0=None, temperature=0, seed=0, step_offset=0, logits=False,
              state=False, lse=False, exec="resident", fixed_latent=False, stream=None, out=None,
-             trace=False):
+             trace=False, noalloc=False):
         """Enqueue one walk.  base: bf16 [B, gamma, V]; x0: int32 [B].
 
         Returns a dict of output tensors (tokens int32 [B, gamma]; logits bf16
@@ -76,7 +76,8 @@ class Head:
         normaliser of each step's logits) and trace int64 [gamma, grid, 4]
         when asked for).  fixed_latent runs the fixed-latent probe (every step
         uses the latent of step 0).  Pass `out` (a dict from an earlier call)
-        to reuse its buffers.
+        to reuse its buffers.  noalloc=True runs the walk through
+        wts_walk_noalloc (scratch in the library's fixed per-GPU array).
         """
         torch = self._torch
         B, gamma, V = base.shape
@@ -99,7 +100,10 @@ class Head:
                             flags=_abi.WALK_FIXED_LATENT if fixed_latent else 0,
                             stream=ctypes.c_void_p(s.cuda_stream), trace_out=_ptr(out.get("trace")),
                             lse_out=_ptr(out.get("lse")))
-        _check(_abi.lib().wts_walk(self._h, ctypes.byref(p)), "wts_walk")
+        if noalloc:
+            _check(_abi.lib().wts_walk_noalloc(self._h, ctypes.byref(p)), "wts_walk_noalloc")
+        else:
+            _check(_abi.lib().wts_walk(self._h, ctypes.byref(p)), "wts_walk")
         return out
 
     def error(self, clear=True):

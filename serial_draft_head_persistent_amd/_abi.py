@@ -19,7 +19,8 @@ EXEC = {"resident": 0, "stream": 1, "stepwise": 2}
 WALK_FIXED_LATENT = 1
 
 EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string",
-           "wts_check_log_ratio"]
+           "wts_check_log_ratio", "wts_walk_noalloc"]
+NOALLOC_LSE_BYTES = 1 << 20
 
 c_int32, c_uint64, c_void_p = ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
 
@@ -71,6 +72,8 @@ def load(path=LIB_PATH):
     lib.wts_create.restype = ctypes.c_int
     lib.wts_walk.argtypes = [c_void_p, P(WalkParams)]
     lib.wts_walk.restype = ctypes.c_int
+    lib.wts_walk_noalloc.argtypes = [c_void_p, P(WalkParams)]
+    lib.wts_walk_noalloc.restype = ctypes.c_int
     lib.wts_destroy.argtypes = [c_void_p]
     lib.wts_destroy.restype = None
     lib.wts_get_error.argtypes = [c_void_p, ctypes.c_int]

@@ -141,5 +141,6 @@ hipError_t launch_finish(const WalkArgs& a, hipStream_t s);
 hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s);
 hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace wts

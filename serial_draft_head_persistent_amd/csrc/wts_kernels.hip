@@ -1950,6 +1950,19 @@ hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s)
   return hipGetLastError();
 }
 
+// Zero `bytes` (a multiple of 16) of device memory with a kernel.
+__global__ void fill_zero_kernel(int4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_int4(0, 0, 0, 0);
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  fill_zero_kernel<<<blocks, 256, 0, s>>>((int4*)p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s) {
   const int pairs = a.B * a.gamma;
   lse_kernel<<<(pairs + kLseWaves - 1) / kLseWaves, kLseWaves * 64, 0, s>>>(a, grid);

@@ -8,6 +8,7 @@
 // streams the rest from memory at every step.
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "wts.h"
@@ -35,7 +36,25 @@ struct wts_ctx {
   long long timeout_ticks = 0;
 };
 
+// Fixed device scratch of wts_walk_noalloc: a control block (exchange lines,
+// step-wise slots, error word) and room for the log-normaliser partials.
+// One copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is a stand-in, not a device
+// address); it uses the per-device address from hipGetSymbolAddress.
+constexpr size_t kNoAllocCtrlBytes = (sizeof(Ctrl) + 255) / 256 * 256;
+constexpr size_t kNoAllocLseBytes = WTS_NOALLOC_LSE_BYTES;
+constexpr size_t kNoAllocBytes = kNoAllocCtrlBytes + kNoAllocLseBytes;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+struct DevScratch {
+  char* ptr = nullptr;            // device address of `scratch` on that GPU
+  unsigned long long walks = 0;   // walks run on it (their parity alternates)
+};
+DevScratch g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
 
 struct DeviceGuard {
   int prev = -1;
@@ -149,6 +168,40 @@ void free_ctx(wts_ctx* ctx) {
   delete ctx;
 }
 
+// Once per device, with that device current: the address of its copy of
+// `scratch`, cleared with a fill kernel (a walk needs its control block at
+// zero before the first call).
+wts_status scratch_init(int device) {
+  if (device >= kMaxDevices) return WTS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[device].ptr) return WTS_OK;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return WTS_ERR_DEVICE;
+  if (launch_fill_zero(ptr, kNoAllocBytes, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return WTS_ERR_DEVICE;
+  g_scratch[device].ptr = (char*)ptr;
+  g_scratch[device].walks = 0;
+  return WTS_OK;
+}
+
+// Reads (and with clear resets) the error word of one control block.
+wts_status read_ctrl_error(Ctrl* ctrl, bool clear, unsigned long long* walks) {
+  unsigned err = 0;
+  if (hipMemcpy(&err, &ctrl->err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return WTS_ERR_DEVICE;
+  if (clear && err) {
+    // A failed walk can leave its slots and counters in any state: start over.
+    if (hipMemset(ctrl, 0, sizeof(Ctrl)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      return WTS_ERR_DEVICE;
+    *walks = 0;
+  }
+  return (wts_status)err;
+}
+
+// One walk with the given control block and log-normaliser partials
+// (lse_cap bytes of room; the context's own, or the device scratch).
+wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap,
+                     unsigned long long* walks);
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +246,8 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   if (cus < 1 || (p->cooperative && !coop)) return WTS_ERR_UNSUPPORTED;
   if (p->cooperative != 0 && p->cooperative != 1) return WTS_ERR_INVALID_ARG;
   if (p->watchdog_us < 0) return WTS_ERR_INVALID_ARG;
+  const wts_status sst = scratch_init(p->device);
+  if (sst != WTS_OK) return sst;
 
   wts_ctx* ctx = new (std::nothrow) wts_ctx();
   if (!ctx) return WTS_ERR_NO_MEMORY;
@@ -262,6 +317,24 @@ wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t tem
 
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   if (!ctx || !p) return WTS_ERR_INVALID_ARG;
+  const size_t groups = (size_t)std::max(ctx->grid, step_grid(ctx));
+  return walk_impl(ctx, p, ctx->ctrl, ctx->lse_part, (size_t)ctx->max_batch * ctx->max_steps * groups * 8,
+                   &ctx->walks);
+}
+
+wts_status wts_walk_noalloc(wts_ctx* ctx, const wts_walk_params* p) {
+  if (!ctx || !p) return WTS_ERR_INVALID_ARG;
+  DevScratch& ds = g_scratch[ctx->device];   // set up by wts_create on this device
+  if (!ds.ptr) return WTS_ERR_DEVICE;
+  return walk_impl(ctx, p, (Ctrl*)ds.ptr, (float*)(ds.ptr + kNoAllocCtrlBytes), kNoAllocLseBytes, &ds.walks);
+}
+
+}  // extern "C"
+
+namespace {
+
+wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap,
+                     unsigned long long* walks) {
   if (p->B < 1 || p->B > ctx->max_batch || p->gamma < 1 || p->gamma > ctx->max_steps) return WTS_ERR_INVALID_ARG;
   if (p->temperature != 0 && p->temperature != 1) return WTS_ERR_INVALID_ARG;
   if (p->step_offset < 0 || (p->flags & ~WTS_WALK_FIXED_LATENT) != 0) return WTS_ERR_INVALID_ARG;
@@ -273,6 +346,11 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
       ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
+  {
+    // room for the (max, sum) pair of every workgroup, row and step
+    const size_t groups = (size_t)(p->exec == WTS_EXEC_STEPWISE ? step_grid(ctx) : ctx->grid);
+    if (p->lse_out && (size_t)p->B * p->gamma * groups * 8 > lse_cap) return WTS_ERR_UNSUPPORTED;
+  }
   DeviceGuard guard(ctx->device);
   const int BB = batch_bucket(p->B);
   wts_plan plan;
@@ -290,7 +368,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.E = ctx->E;
   a.A = ctx->A;
   a.c = ctx->c;
-  a.ctrl = ctx->ctrl;
+  a.ctrl = ctrl;
   a.V = ctx->V;
   a.tiles = ctx->tiles;
   a.head = ctx->head;
@@ -304,7 +382,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.temperature = p->temperature;
   a.seed_lo = (unsigned)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (unsigned)(p->seed >> 32);
-  a.parity = (int)(ctx->walks & 1ull);
+  a.parity = (int)(*walks & 1ull);
   a.base = p->base;
   a.x0 = p->x0;
   a.h0 = p->h0;
@@ -316,7 +394,7 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   a.fixed_latent = (p->flags & WTS_WALK_FIXED_LATENT) != 0;
   a.full = full;
   a.lse = p->lse_out;
-  a.lse_part = ctx->lse_part;
+  a.lse_part = lse_part;
   hipStream_t s = (hipStream_t)p->stream;
 
   hipError_t e;
@@ -334,23 +412,26 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
     if (e == hipSuccess && a.lse) e = launch_lse(a, ctx->grid, s);
   }
   if (e != hipSuccess) return WTS_ERR_DEVICE;
-  ctx->walks++;
+  ++*walks;
   return WTS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 wts_status wts_get_error(wts_ctx* ctx, int clear) {
   if (!ctx) return WTS_ERR_INVALID_ARG;
   DeviceGuard guard(ctx->device);
   if (hipDeviceSynchronize() != hipSuccess) return WTS_ERR_DEVICE;
-  unsigned err = 0;
-  if (hipMemcpy(&err, &ctx->ctrl->err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return WTS_ERR_DEVICE;
-  if (clear && err) {
-    // A failed walk can leave its slots and counters in any state: start over.
-    if (hipMemset(ctx->ctrl, 0, sizeof(Ctrl)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-      return WTS_ERR_DEVICE;
-    ctx->walks = 0;
+  wts_status st = read_ctrl_error(ctx->ctrl, clear != 0, &ctx->walks);
+  // walks through wts_walk_noalloc latch into the device scratch
+  DevScratch& ds = g_scratch[ctx->device];
+  if (ds.ptr) {
+    const wts_status s2 = read_ctrl_error((Ctrl*)ds.ptr, clear != 0, &ds.walks);
+    if (st == WTS_OK) st = s2;
   }
-  return (wts_status)err;
+  return st;
 }
 
 wts_status wts_check_log_ratio(int32_t device, int64_t* mismatches) {
