@@ -95,6 +95,14 @@ typedef struct wts_create_params {
                              microseconds (>= 1), of every wait inside a walk;
                              a wait that exceeds it latches WTS_ERR_TIMEOUT and
                              its workgroup exits.                              */
+  int32_t grid;           /* 0: one workgroup per compute unit (at most 256).
+                             Otherwise that many workgroups (1..256, at most
+                             the compute units), each with a larger shard.   */
+  int32_t exchange;       /* Cross-workgroup selection (Fig. 8).  0: the first
+                             level (16 groups) runs through one XCD's L2 when
+                             a create-time check finds workgroup g dispatched
+                             to the same XCD as g mod 16, else device scope.
+                             1: device scope at both levels.                   */
 } wts_create_params;
 
 typedef struct wts_walk_params {
@@ -138,16 +146,23 @@ typedef struct wts_plan {
   int64_t resident_bytes;  /* W bytes on chip over the whole GPU               */
   int64_t streamed_bytes;  /* W bytes read from memory per step                */
   int64_t w_bytes;         /* V * r * element size                             */
+  int32_t exchange;        /* 0: first selection level inside an XCD's L2;
+                              1: device scope (see wts_create_params.exchange)  */
 } wts_plan;
 
 /* Create a head: validates, plans residency, and copies W into a tile-major
  * layout owned by the context (plus the quantised embedding rows, Fig. 7).
- * Borrows E, A, c: keep them alive until wts_destroy.  Synchronous. */
+ * Borrows E, A, c: keep them alive until wts_destroy.  Synchronous.
+ * WTS_ERR_UNSUPPORTED if a workgroup would own more than 65,535 vocabulary
+ * rows (V / grid; the local selection key holds a 16-bit row). */
 wts_status wts_create(const wts_create_params* p, wts_ctx** out);
 
 /* Enqueue one walk on p->stream (asynchronous; inputs must stay alive and
  * unmodified until the stream reaches the walk's end).  Writes tokens_out
- * [b][t] = token chosen at step t, and optionally logits_out and state_out. */
+ * [b][t] = token chosen at step t, and optionally logits_out and state_out.
+ * WTS_ERR_UNSUPPORTED (before any launch) if the LDS a T=1 Markov walk needs
+ * for one step of Gumbel noise (4 bytes per batch row and vocabulary row of a
+ * workgroup) does not fit beside the kernel's other LDS data. */
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p);
 
 /* For callers that cannot allocate device memory (code under HIP graph

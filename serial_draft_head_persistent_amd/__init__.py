@@ -35,11 +35,14 @@ class Head:
     W: int8 [V, 256] (with w_scale float32 [V]) or bf16 [V, 256]; E float32
     [V, 256]; recurrent heads also take A bf16 [256, 256] and c float32 [256].
     All tensors live on the same CUDA (HIP) device and are borrowed until
-    close().
+    close().  grid: workgroups of the persistent walk (0: one per compute
+    unit).  exchange: "auto" (the first selection level inside one XCD when
+    the create-time dispatch check passes) or "device" (device scope).
     """
 
     def __init__(self, W, E, *, w_scale=None, A=None, c=None, head="markov", max_batch=16,
-                 max_steps=64, resident_tiles=-1, lds_tiles=-1, cooperative=False, watchdog_us=0):
+                 max_steps=64, resident_tiles=-1, lds_tiles=-1, cooperative=False, watchdog_us=0, grid=0,
+                 exchange="auto"):
         import torch
         self._torch = torch
         wtype = "int8" if W.dtype == torch.int8 else "bf16"
@@ -56,7 +59,8 @@ class Head:
                               w_scale=_ptr(w_scale), E=_ptr(E), A=_ptr(A), c=_ptr(c), max_batch=max_batch,
                               max_steps=max_steps, resident_tiles=resident_tiles, lds_tiles=lds_tiles,
                               device=W.device.index or 0, cooperative=int(bool(cooperative)),
-                              watchdog_us=watchdog_us)
+                              watchdog_us=watchdog_us, grid=grid,
+                              exchange={"auto": 0, "device": 1}[exchange])
         h = ctypes.c_void_p()
         _check(_abi.lib().wts_create(ctypes.byref(p), ctypes.byref(h)), "wts_create")
         self._h = h

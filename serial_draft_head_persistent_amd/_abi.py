@@ -30,7 +30,7 @@ class CreateParams(ctypes.Structure):
                 ("W", c_void_p), ("w_scale", c_void_p), ("E", c_void_p), ("A", c_void_p), ("c", c_void_p),
                 ("max_batch", c_int32), ("max_steps", c_int32), ("resident_tiles", c_int32),
                 ("lds_tiles", c_int32), ("device", c_int32), ("cooperative", c_int32),
-                ("watchdog_us", c_int32)]
+                ("watchdog_us", c_int32), ("grid", c_int32), ("exchange", c_int32)]
 
 
 class WalkParams(ctypes.Structure):
@@ -45,7 +45,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("grid", c_int32), ("waves", c_int32), ("tiles", c_int32), ("tiles_per_wave", c_int32),
                 ("reg_tiles", c_int32), ("lds_tiles", c_int32), ("stream_tiles", c_int32),
                 ("resident_bytes", ctypes.c_int64), ("streamed_bytes", ctypes.c_int64),
-                ("w_bytes", ctypes.c_int64)]
+                ("w_bytes", ctypes.c_int64), ("exchange", c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

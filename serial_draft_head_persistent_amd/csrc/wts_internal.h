@@ -126,6 +126,7 @@ struct WalkArgs {
   int full;                // whole shard on chip (reg_tiles_full variant); lds tiles allotted per wave
   float* lse;              // [B][gamma] log normaliser per step, or null
   float* lse_part;         // [B][gamma][grid] (max, sum) pairs of the workgroups (scratch)
+  int xcd_l1;              // 1: first exchange level inside one XCD's L2; 0: device scope
 };
 
 // Launchers (wts_kernels.hip).  Each returns the HIP error of its launch.
@@ -142,5 +143,6 @@ hipError_t launch_lse(const WalkArgs& a, int grid, hipStream_t s);
 hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s);
 hipError_t prepare_kernels(int lds_bytes);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_xcc_ids(unsigned* out, int grid, hipStream_t s);
 
 }  // namespace wts

@@ -943,9 +943,13 @@ __device__ __forceinline__ void st_agent(unsigned long long* p, unsigned long lo
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Signalling inside one XCD through its shared L2: a plain store (the CU's
-// L1 writes through to the L2) and a non-temporal load, which the L1 does not
-// serve from a retained line.  About 0.28 us one way on MI355X, against
-// 0.47 us for the device-scope pair above, which bypasses the L2.
+// L1 writes through to the L2) and a load with the non-temporal bit (NT=1)
+// at the default scope.  For such a load the vector L1 applies its streaming
+// policy and keeps no copy of the line, so every poll is served by the L2,
+// where the other workgroups of the XCD store.  About 0.28 us one way on
+// MI355X, against 0.47 us for the device-scope pair above, which bypasses the
+// L2.  (Were a polled line kept in L1, the poll would never see the new key,
+// and the watchdog would latch a time-out rather than a wrong token.)
 __device__ __forceinline__ void st_xcd(unsigned long long* p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -1029,24 +1033,27 @@ __device__ __forceinline__ unsigned long long class_max(unsigned long long x) {
 // waits for its members' keys and publishes the group maximum in kCopies
 // copies; every workgroup waits for the kGroups group maxima in copy
 // (g % kCopies) and takes the overall maximum.  Workgroups are dispatched
-// round-robin over the XCDs (g % 8 on MI355X), so a group (g % kGroups) lies
-// on one XCD: its keys travel through that XCD's L2 (st_xcd / ld_xcd), and
-// only the group maxima cross XCDs (device scope, one copy per XCD).  Were a
-// member on another XCD, its leader would not see the key and the watchdog
-// would latch a timeout; a stale line never passes for a new one, since every
-// key carries its step.  The keys carry the token, so no other data has to be
+// round-robin over the XCDs (g % 8 on MI355X; the host checks this at create
+// time), so a group (g % kGroups) lies on one XCD and, with xl1, its keys
+// travel through that XCD's L2 (st_xcd / ld_xcd); only the group maxima cross
+// XCDs (device scope, one copy per XCD).  Without xl1 (the dispatch check
+// failed, or the caller asked for it) the first level uses device scope too.
+// A stale line never passes for a new one, since every key carries its step.  The keys carry the token, so no other data has to be
 // made visible: relaxed loads and stores suffice.  Returns false if the
 // watchdog expired.  On return, lanes b < B hold the winning key of row b.
 template <int BB, bool CAND>
 __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsigned long long key,
-                                         long long timeout, unsigned long long* winner, char* lds) {
+                                         long long timeout, unsigned long long* winner, char* lds, bool xl1) {
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x, G = gridDim.x;
   const unsigned long long want = (unsigned long long)(t + 1);
   const unsigned long long tag = want << kTagShift;
   unsigned long long* L1 = &ctrl->l1[par][t & 1][0][0];
   unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0][0];
-  if (lane < B) st_xcd(&L1[g * kMaxB + lane], tag | key);
+  if (lane < B) {
+    if (xl1) st_xcd(&L1[g * kMaxB + lane], tag | key);
+    else st_agent(&L1[g * kMaxB + lane], tag | key);
+  }
   const int grp = g % kGroups;
   const long long t0 = wall_clock64();
   bool ok_all = true;
@@ -1065,7 +1072,12 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     unsigned long long best;
     while (true) {
       unsigned long long v[NQ];
-      ld_xcd<NQ>(pp, v);
+      if (xl1) {
+        ld_xcd<NQ>(pp, v);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) v[k] = ld_agent(pp[k]);
+      }
       bool ok = true;
       best = 0ull;
 #pragma unroll
@@ -1715,7 +1727,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         k = global_key(lk, row0);
       }
       unsigned long long win;
-      const bool ok = exchange<BB, CAND>(ctrl, par, t, a.B, k, a.timeout_ticks, &win, lds);
+      const bool ok = exchange<BB, CAND>(ctrl, par, t, a.B, k, a.timeout_ticks, &win, lds, a.xcd_l1 != 0);
       if (!ok && lane == 0) {
         latch_error(ctrl, 5u);
         *sflag = 1;
@@ -1947,6 +1959,17 @@ __global__ __launch_bounds__(256) void check_log_ratio_kernel(unsigned long long
 
 hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s) {
   check_log_ratio_kernel<<<(1u << 23) / 256, 256, 0, s>>>(mismatches);
+  return hipGetLastError();
+}
+
+// XCD (XCC) that workgroup g runs on, from the hardware register XCC_ID
+// (bits 3:0), one entry per workgroup.
+__global__ void xcc_id_kernel(unsigned* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = (unsigned)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xFu;
+}
+
+hipError_t launch_xcc_ids(unsigned* out, int grid, hipStream_t s) {
+  xcc_id_kernel<<<grid, 64, 0, s>>>(out);
   return hipGetLastError();
 }
 

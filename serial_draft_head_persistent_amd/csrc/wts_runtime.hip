@@ -22,6 +22,7 @@ struct wts_ctx {
   int max_batch = 0, max_steps = 0;
   int reg_cap = -1, lds_cap = -1;
   bool cooperative = false;
+  bool xcd_l1 = false;  // first exchange level inside one XCD's L2
   int4* Wp = nullptr;
   float* sw = nullptr;
   int8_t* Eq = nullptr;
@@ -92,7 +93,9 @@ int wave_tiles(int cnt, int w, int NW) { return cnt > w ? (cnt - w + NW - 1) / N
 
 // Residency plan for one batch bucket.  *full: the whole shard fits on chip
 // in the variant with more register tiles and LDS tiles allotted per wave.
-void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, wts_plan* p, int* lds_bytes,
+// Returns false if the kernel's LDS scratch (with the T=1 noise of one step)
+// does not fit in LDS.
+bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, wts_plan* p, int* lds_bytes,
                int* noise_off = nullptr, int* noise_stride = nullptr, int* full = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
   const int NW = waves_for(ctx->head, ctx->wtype);
@@ -144,7 +147,29 @@ void make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, 
   p->w_bytes = (long long)ctx->V * kR * esz;
   p->resident_bytes = res_tiles * tb;
   p->streamed_bytes = (long long)ctx->tiles * tb - p->resident_bytes;
+  p->exchange = ctx->xcd_l1 ? 0 : 1;
   *lds_bytes = std::min(kLdsMax, std::max(scratch + lds_need * tb, 96 * 1024));
+  return scratch <= kLdsMax;
+}
+
+// Whether workgroup g of a grid of `grid` runs on the same XCD as workgroup
+// g % kGroups (the first level of the exchange keeps each group inside one
+// XCD's L2).  Reads every workgroup's XCC_ID once.
+wts_status check_xcd_groups(int grid, bool* same) {
+  *same = false;
+  unsigned* d = nullptr;
+  if (hipMalloc((void**)&d, kMaxGrid * sizeof(unsigned)) != hipSuccess) return WTS_ERR_NO_MEMORY;
+  unsigned h[kMaxGrid];
+  wts_status st = WTS_OK;
+  if (launch_xcc_ids(d, grid, 0) != hipSuccess ||
+      hipMemcpy(h, d, grid * sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+    st = WTS_ERR_DEVICE;
+  (void)hipFree(d);
+  if (st != WTS_OK) return st;
+  bool ok = true;
+  for (int g = 0; g < grid; ++g) ok = ok && h[g] == h[g % kGroups];
+  *same = ok;
+  return WTS_OK;
 }
 
 template <class T>
@@ -234,6 +259,7 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   if (p->resident_tiles < -1 || p->lds_tiles < -1) return WTS_ERR_INVALID_ARG;
   if (((uintptr_t)p->W & 15) || ((uintptr_t)p->E & 15) || ((uintptr_t)p->A & 15) || ((uintptr_t)p->c & 3))
     return WTS_ERR_INVALID_ARG;
+  if (p->grid < 0 || p->grid > kMaxGrid || (p->exchange != 0 && p->exchange != 1)) return WTS_ERR_INVALID_ARG;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev) return WTS_ERR_INVALID_ARG;
   DeviceGuard guard(p->device);
@@ -246,6 +272,13 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   if (cus < 1 || (p->cooperative && !coop)) return WTS_ERR_UNSUPPORTED;
   if (p->cooperative != 0 && p->cooperative != 1) return WTS_ERR_INVALID_ARG;
   if (p->watchdog_us < 0) return WTS_ERR_INVALID_ARG;
+  if (p->grid > cus) return WTS_ERR_INVALID_ARG;
+  {
+    // the workgroup-local selection key holds a 16-bit row (V / grid rows at most)
+    const int g = p->grid ? p->grid : std::min(cus, kMaxGrid);
+    const long long tiles = (p->V + kTileRows - 1) / kTileRows;
+    if ((tiles + g - 1) / g * kTileRows > 65535) return WTS_ERR_UNSUPPORTED;
+  }
   const wts_status sst = scratch_init(p->device);
   if (sst != WTS_OK) return sst;
 
@@ -256,7 +289,7 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   ctx->head = p->head;
   ctx->wtype = p->wtype;
   ctx->tiles = (p->V + kTileRows - 1) / kTileRows;
-  ctx->grid = std::min(cus, kMaxGrid);
+  ctx->grid = p->grid ? p->grid : std::min(cus, kMaxGrid);
   ctx->cooperative = p->cooperative != 0;
   ctx->max_batch = p->max_batch;
   ctx->max_steps = p->max_steps;
@@ -302,6 +335,15 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
     free_ctx(ctx);
     return WTS_ERR_DEVICE;
   }
+  if (p->exchange == 0) {
+    bool same = false;
+    const wts_status xs = check_xcd_groups(ctx->grid, &same);
+    if (xs != WTS_OK) {
+      free_ctx(ctx);
+      return xs;
+    }
+    ctx->xcd_l1 = same;
+  }
   *out = ctx;
   return WTS_OK;
 }
@@ -311,8 +353,8 @@ wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t tem
   if (exec < WTS_EXEC_RESIDENT || exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
   if (temperature != 0 && temperature != 1) return WTS_ERR_INVALID_ARG;
   int lds_bytes = 0;
-  make_plan(ctx, batch_bucket(B), exec, temperature, false, out, &lds_bytes);
-  return WTS_OK;
+  return make_plan(ctx, batch_bucket(B), exec, temperature, false, out, &lds_bytes) ? WTS_OK
+                                                                                     : WTS_ERR_UNSUPPORTED;
 }
 
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
@@ -356,8 +398,9 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   wts_plan plan;
   int lds_bytes = 0;
   int noise_off = 0, noise_stride = 0, full = 0;
-  make_plan(ctx, BB, p->exec, p->temperature, p->lse_out != nullptr, &plan, &lds_bytes, &noise_off, &noise_stride,
-            &full);
+  if (!make_plan(ctx, BB, p->exec, p->temperature, p->lse_out != nullptr, &plan, &lds_bytes, &noise_off,
+                 &noise_stride, &full))
+    return WTS_ERR_UNSUPPORTED;
 
   WalkArgs a{};
   a.Wp = ctx->Wp;
@@ -395,6 +438,7 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   a.full = full;
   a.lse = p->lse_out;
   a.lse_part = lse_part;
+  a.xcd_l1 = ctx->xcd_l1 ? 1 : 0;
   hipStream_t s = (hipStream_t)p->stream;
 
   hipError_t e;

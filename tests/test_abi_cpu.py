@@ -75,7 +75,8 @@ def _valid_create_params(_abi):
     ("V", 0, 1), ("V", 262144, 1), ("r", 0, 1), ("r", 128, 2), ("head", 2, 1), ("wtype", 2, 1),
     ("W", None, 1), ("E", None, 1), ("w_scale", None, 1), ("max_batch", 0, 1), ("max_batch", 17, 1),
     ("max_steps", 0, 1), ("max_steps", 65, 1), ("resident_tiles", -2, 1), ("lds_tiles", -2, 1),
-    ("W", 0x7F0000000008, 1), ("E", 0x7F0000000004, 1),
+    ("W", 0x7F0000000008, 1), ("E", 0x7F0000000004, 1), ("grid", -1, 1), ("grid", 257, 1),
+    ("exchange", 2, 1), ("exchange", -1, 1),
 ])
 def test_create_rejects_bad_arguments_before_any_device_call(field, value, status):
     """Host-detectable errors of wts_create return a status (1 = invalid
