@@ -160,6 +160,9 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out);
 /* Enqueue one walk on p->stream (asynchronous; inputs must stay alive and
  * unmodified until the stream reaches the walk's end).  Writes tokens_out
  * [b][t] = token chosen at step t, and optionally logits_out and state_out.
+ * The walk keeps no host-side state between calls (the control block's
+ * parity advances on the device), so a walk captured in a HIP graph may be
+ * replayed; the captured pointers' contents may change between replays.
  * WTS_ERR_UNSUPPORTED (before any launch) if the LDS a T=1 Markov walk needs
  * for one step of Gumbel noise (4 bytes per batch row and vocabulary row of a
  * workgroup) does not fit beside the kernel's other LDS data. */

@@ -9,7 +9,7 @@ import ctypes
 from . import _abi
 from ._abi import WtsError, EXEC, HEAD, WTYPE  # noqa: F401
 
-__all__ = ["Head", "WtsError", "check_log_ratio"]
+__all__ = ["Head", "WtsError", "check_log_ratio", "roofline"]
 
 
 def check_log_ratio(device=0):
@@ -18,6 +18,16 @@ def check_log_ratio(device=0):
     n = ctypes.c_int64(-1)
     _check(_abi.lib().wts_check_log_ratio(int(device), ctypes.byref(n)), "wts_check_log_ratio")
     return n.value
+
+
+def roofline(device=0):
+    """Measured roofline denominators on `device` (wts_roofline): LDS read and
+    MFMA issue rates, shader clock, HBM and memory-side-cache stream rates, the
+    cross-workgroup selection round of four exchange designs, one-way signal
+    hops and VALU issue cycles.  Returns a dict."""
+    r = _abi.RooflineResult()
+    _check(_abi.lib().wts_roofline(int(device), ctypes.byref(r)), "wts_roofline")
+    return r.as_dict()
 
 
 def _ptr(t):

@@ -21,6 +21,8 @@ WALK_FIXED_LATENT = 1
 EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string",
            "wts_check_log_ratio", "wts_walk_noalloc"]
 NOALLOC_LSE_BYTES = 1 << 20
+# include/wts_roofline.h (measured roofline denominators)
+ROOFLINE_EXPORTS = ["wts_roofline"]
 
 c_int32, c_uint64, c_void_p = ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
 
@@ -49,6 +51,25 @@ class Plan(ctypes.Structure):
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class RooflineResult(ctypes.Structure):
+    _fields_ = [("grid", c_int32), ("pad", c_int32), ("lds_read_GBps", ctypes.c_double),
+                ("mfma_i8_TOPs", ctypes.c_double), ("mfma_bf16_TFLOPs", ctypes.c_double),
+                ("clock_MHz", ctypes.c_double), ("hbm_read_GBps", ctypes.c_double),
+                ("mall_read_GBps", ctypes.c_double), ("exchange_us", ctypes.c_double * 6),
+                ("exchange_bad", ctypes.c_int64 * 6), ("hop_xcd_us", ctypes.c_double),
+                ("hop_device_us", ctypes.c_double), ("valu_dep_cycles", ctypes.c_double),
+                ("valu_indep_cycles", ctypes.c_double), ("valu_indep_2w_cycles", ctypes.c_double),
+                ("valu_indep_4w_cycles", ctypes.c_double)]
+
+    def as_dict(self):
+        out = {}
+        for k, _ in self._fields_:
+            v = getattr(self, k)
+            out[k] = list(v) if hasattr(v, "__len__") else v
+        out.pop("pad")
+        return out
 
 
 class WtsError(RuntimeError):
@@ -84,6 +105,8 @@ def load(path=LIB_PATH):
     lib.wts_status_string.restype = ctypes.c_char_p
     lib.wts_check_log_ratio.argtypes = [c_int32, P(ctypes.c_int64)]
     lib.wts_check_log_ratio.restype = ctypes.c_int
+    lib.wts_roofline.argtypes = [c_int32, P(RooflineResult)]
+    lib.wts_roofline.restype = ctypes.c_int
     return lib
 
 

@@ -26,7 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwts.so")
 RESOURCES = os.path.join(PKG, "libwts.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["wts_kernels.hip", "wts_runtime.hip"]
+SOURCES = ["wts_kernels.hip", "wts_runtime.hip", "wts_roofline.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
@@ -66,7 +66,7 @@ def parse_resources(text):
     return out
 
 
-def build(verbose=False, jobs=2):
+def build(verbose=False, jobs=3):
     objs = []
     procs = []
     for src in SOURCES:

@@ -74,9 +74,12 @@ constexpr int kCopies = 8;      // copies of the second-level lines (one per XCD
 constexpr int kSub = 16;        // step-wise path: sub-slots per (step, batch row)
 
 // Device control block of one context.  Every array has a leading walk
-// parity: walk k uses parity k & 1, and the first launch of walk k clears
-// the arrays of parity (k + 1) & 1 for the next walk, so no host-side reset
-// is needed between walks.
+// parity: a walk reads `epoch` when it starts and uses parity epoch & 1, its
+// first launch clears the arrays of the other parity for the next walk, and
+// its last act advances `epoch` (the persistent walk: workgroup 0 after its
+// last exchange; the step-wise walk: its finishing launch).  No host-side
+// state or reset is needed between walks, so a walk captured once in a graph
+// can be replayed.
 struct Ctrl {
   // persistent walk, two-level all-gather of tagged keys (step parity second)
   unsigned long long l1[2][2][kMaxGrid][kMaxB];   // one line per workgroup
@@ -84,7 +87,8 @@ struct Ctrl {
   // step-wise walk: device-scope max per (step, batch row, sub-slot)
   unsigned long long ss[2][kMaxSteps][kMaxB][kSub];
   unsigned int err;                               // latched wts_status
-  unsigned int pad[63];
+  unsigned int epoch;                             // walks completed (their parity alternates)
+  unsigned int pad[62];
 };
 
 struct WalkArgs {
@@ -112,7 +116,6 @@ struct WalkArgs {
   int temperature;
   unsigned seed_lo;
   unsigned seed_hi;
-  int parity;
   int step;                // step-wise launches: the step this launch runs
   const uint16_t* base;
   const int* x0;
@@ -144,5 +147,14 @@ hipError_t launch_check_log_ratio(unsigned long long* mismatches, hipStream_t s)
 hipError_t prepare_kernels(int lds_bytes);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_xcc_ids(unsigned* out, int grid, hipStream_t s);
+// roofline microbenchmarks (wts_roofline.hip drives them)
+hipError_t launch_rf_lds(int grid, int rounds, unsigned* out, hipStream_t s);
+hipError_t launch_rf_mfma(int wtype, int grid, int rounds, unsigned* out, long long* clk, hipStream_t s);
+hipError_t launch_rf_stream(const void* p, long long n16, int passes, int grid, unsigned* out, hipStream_t s);
+hipError_t launch_rf_exchange(int variant, int grid, int rounds, Ctrl* ctrl, unsigned long long* flat, unsigned* cnt,
+                              long long timeout, long long* clk, unsigned* wrong, hipStream_t s);
+hipError_t launch_rf_pingpong(int grid, int peer, int xcd, int rounds, unsigned long long* flag, long long timeout,
+                              long long* clk, hipStream_t s);
+hipError_t launch_rf_valu(bool dep, int waves, int n, float* out, long long* clk, hipStream_t s);
 
 }  // namespace wts

@@ -936,6 +936,17 @@ __device__ __forceinline__ void latch_error(Ctrl* ctrl, unsigned code) {
   atomicCAS(&ctrl->err, 0u, code);
 }
 
+// Parity of the walk that reads it (every launch of one walk reads the same
+// epoch: the walk advances it only at its very end).
+__device__ __forceinline__ int walk_parity(Ctrl* ctrl) {
+  // one value for the whole wave, held in a scalar register
+  return __builtin_amdgcn_readfirstlane(
+      (int)(__hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u));
+}
+__device__ __forceinline__ void advance_epoch(Ctrl* ctrl) {
+  __hip_atomic_fetch_add(&ctrl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ unsigned long long ld_agent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -987,10 +998,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the whole grid.  Nothing in this walk touches them.  OWN_L1: each
 // workgroup clears its own first-level lines (the persistent walk, whose
 // first level stays inside an XCD); otherwise the grid clears all of them.
-template <bool OWN_L1>
+template <bool OWN_L1, bool PACKED = false>
 __device__ __forceinline__ void clear_next_walk(Ctrl* ctrl, int par) {
   const int q = par ^ 1;
-  if (OWN_L1 && threadIdx.x < 2 * kMaxB) ctrl->l1[q][threadIdx.x / kMaxB][blockIdx.x][threadIdx.x % kMaxB] = 0ull;
+  if (OWN_L1 && threadIdx.x < 2 * kMaxB) {
+    const int g = blockIdx.x, b = threadIdx.x % kMaxB;
+    const int at = PACKED ? ((g % kGroups) * kMaxB + b) * kGroups + g / kGroups : g * kMaxB + b;
+    (&ctrl->l1[q][threadIdx.x / kMaxB][0][0])[at] = 0ull;
+  }
   const size_t n1 = OWN_L1 ? 0 : sizeof(ctrl->l1[0]) / 8, n2 = sizeof(ctrl->l2[0]) / 8, n3 = sizeof(ctrl->ss[0]) / 8;
   unsigned long long* p1 = &ctrl->l1[q][0][0][0];
   unsigned long long* p2 = &ctrl->l2[q][0][0][0][0];
@@ -1041,7 +1056,10 @@ __device__ __forceinline__ unsigned long long class_max(unsigned long long x) {
 // A stale line never passes for a new one, since every key carries its step.  The keys carry the token, so no other data has to be
 // made visible: relaxed loads and stores suffice.  Returns false if the
 // watchdog expired.  On return, lanes b < B hold the winning key of row b.
-template <int BB, bool CAND>
+// PACKED: the keys one poll reads share 128-byte lines -- first level
+// [group][row][member], second level [copy][row][group] -- instead of one
+// line per workgroup and per group.
+template <int BB, bool CAND, bool PACKED = false>
 __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsigned long long key,
                                          long long timeout, unsigned long long* winner, char* lds, bool xl1) {
   const int lane = threadIdx.x & 63;
@@ -1050,11 +1068,14 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
   const unsigned long long tag = want << kTagShift;
   unsigned long long* L1 = &ctrl->l1[par][t & 1][0][0];
   unsigned long long* L2 = &ctrl->l2[par][t & 1][0][0][0];
-  if (lane < B) {
-    if (xl1) st_xcd(&L1[g * kMaxB + lane], tag | key);
-    else st_agent(&L1[g * kMaxB + lane], tag | key);
-  }
   const int grp = g % kGroups;
+  // line index of member i's key of row b (group grp), and of group x's maximum of row b in copy c
+  auto l1_at = [&](int i, int b) { return PACKED ? (grp * kMaxB + b) * kGroups + i : (grp + kGroups * i) * kMaxB + b; };
+  auto l2_at = [&](int c, int x, int b) { return PACKED ? (c * kMaxB + b) * kGroups + x : (c * kGroups + x) * kMaxB + b; };
+  if (lane < B) {
+    if (xl1) st_xcd(&L1[l1_at(g / kGroups, lane)], tag | key);
+    else st_agent(&L1[l1_at(g / kGroups, lane)], tag | key);
+  }
   const long long t0 = wall_clock64();
   bool ok_all = true;
   if (g < kGroups) {
@@ -1067,7 +1088,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
     for (int k = 0; k < NQ; ++k) {
       const int q = lane + 64 * k, i = q / BB, b = q % BB;
       act[k] = q < nmem * BB && b < B;
-      pp[k] = act[k] ? &L1[(grp + kGroups * i) * kMaxB + b] : &L1[g * kMaxB];  // idle lanes: own line
+      pp[k] = act[k] ? &L1[l1_at(i, b)] : &L1[l1_at(g / kGroups, 0)];  // idle lanes: own key
     }
     unsigned long long best;
     while (true) {
@@ -1097,7 +1118,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
       // after class_max every lane holds the maximum of batch row (lane % BB)
       for (int q = lane; q < kCopies * BB; q += 64) {
         const int r = q / BB, b = q % BB;
-        if (b < B) st_agent(&L2[(r * kGroups + grp) * kMaxB + b], best);
+        if (b < B) st_agent(&L2[l2_at(r, grp, b)], best);
       }
     }
   }
@@ -1111,7 +1132,7 @@ __device__ __forceinline__ bool exchange(Ctrl* ctrl, int par, int t, int B, unsi
   for (int k = 0; k < NQ2; ++k) {
     const int q = lane + 64 * k, x = q / BB, b = q % BB;
     act2[k] = q < ngr * BB && b < B;
-    p2[k] = &L2[((g % kCopies) * kGroups + (act2[k] ? x : 0)) * kMaxB + (act2[k] ? b : 0)];
+    p2[k] = &L2[l2_at(g % kCopies, act2[k] ? x : 0, act2[k] ? b : 0)];
   }
   unsigned long long best = 0ull;
   while (ok_all) {
@@ -1428,7 +1449,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   const int nreg = min(nw, a.reg_tiles);
   const int nlds = FULL ? min(nw - nreg, kFullLdsMax) : min(nw - nreg, a.lds_tiles);
   Ctrl* ctrl = a.ctrl;
-  const int par = a.parity;
+  const int par = walk_parity(ctrl);
   constexpr bool CAND = stage_candidates(HEAD, WT, BB);
   constexpr bool NOISE = TEMP && HEAD == kHeadMarkov;  // noise one step ahead in LDS
   // fixed-latent probe (Fig. 13b): the state is never advanced after step 0
@@ -1749,6 +1770,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     __syncthreads();
     if (*sflag) return;
   }
+  // Workgroup 0 has finished its last exchange, so every workgroup has read
+  // the epoch: the next walk may use the other parity.
+  if (g == 0 && tid == 0) advance_epoch(ctrl);
   if (HEAD == kHeadRecurrent && g == 0 && a.state) {
     const float* h = (const float*)(lds + kOffH);
     for (int i = tid; i < a.B * kR; i += NT) a.state[i] = h[i];
@@ -1772,7 +1796,7 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   const int g = blockIdx.x, G = gridDim.x;
   const int t = a.step;
   Ctrl* ctrl = a.ctrl;
-  const int par = a.parity;
+  const int par = walk_parity(ctrl);
   if (t == 0) clear_next_walk<false>(ctrl, par);
   if (tid < a.B) {
     int x = a.x0[tid];
@@ -1830,15 +1854,18 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(WalkArgs a) {
   }
 }
 
-// Last token of a step-wise walk.
+// Last token of a step-wise walk; then the walk's epoch advances.
 __global__ void finish_kernel(WalkArgs a) {
   const int b = threadIdx.x;
+  const int par = walk_parity(a.ctrl);
   if (b < a.B) {
     unsigned long long k = 0ull;
-    for (int i = 0; i < kSub; ++i) k = umax64(k, ld_agent(&a.ctrl->ss[a.parity][a.gamma - 1][b][i]));
+    for (int i = 0; i < kSub; ++i) k = umax64(k, ld_agent(&a.ctrl->ss[par][a.gamma - 1][b][i]));
     const int x = key_token(k);
     a.tokens[b * a.gamma + a.gamma - 1] = (x >= 0 && x < a.V) ? x : 0;
   }
+  __syncthreads();
+  if (b == 0) advance_epoch(a.ctrl);
 }
 
 // ----------------------------------------------------------------------------
@@ -2030,6 +2057,304 @@ static hipError_t set_lds_attr_all(int lds_bytes) {
 hipError_t prepare_kernels(int lds_bytes) {
   const hipError_t e = set_lds_attr_all<false>(lds_bytes);
   return e != hipSuccess ? e : set_lds_attr_all<true>(lds_bytes);
+}
+
+
+// ----------------------------------------------------------------------------
+// roofline microbenchmarks: the denominators of the walk's rooflines,
+// measured on the device the walk runs on (one workgroup per CU where the
+// walk has one)
+// ----------------------------------------------------------------------------
+
+// Aggregate LDS read rate: every lane reads 16 bytes per ds_read_b128 from
+// its own consecutive chunk (no bank conflicts), 8 reads in flight per round;
+// the round's offset is made opaque so that no read can leave the loop.
+__global__ __launch_bounds__(512) void rf_lds_kernel(int rounds, unsigned* out) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 65536 / 16; i += blockDim.x) ((int4*)lds)[i] = make_int4(i, i ^ 1, i ^ 2, i ^ 3);
+  __syncthreads();
+  v4i acc = {0, 0, 0, 0};
+  typedef const __attribute__((address_space(3))) v4i lds_v4i;
+  for (int r = 0; r < rounds; ++r) {
+    int base = ((r & 7) * 8192 + tid * 16) & 65535;
+    asm volatile("" : "+v"(base));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= *(lds_v4i*)(lds + ((base + u * 8192) & 65535));
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678) out[blockIdx.x] = 1u;
+}
+
+// Dense MFMA issue rate: 8 independent accumulator chains per wave with
+// register operands.  Thread 0 of each workgroup also records the shader
+// clock (s_memtime) and the 100 MHz wall clock at the start and the end.
+template <int WT>
+__global__ __launch_bounds__(512) void rf_mfma_kernel(int rounds, unsigned* out, long long* clk) {
+  using AT = typename AccT<WT>::T;
+  const int lane = threadIdx.x & 63;
+  v4i a = {lane, lane * 3, lane * 5, lane * 7}, b = {lane * 11, lane * 13, lane ^ 7, lane ^ 9};
+  if (WT == 1) {  // small bf16 values (no overflow): bit patterns of numbers near 1
+    a = v4i{0x3F803F80, 0x3F813F82, 0x3F833F84, 0x3F853F86};
+    b = v4i{0x3F873F88, 0x3F893F8A, 0x3F8B3F8C, 0x3F8D3F8E};
+  }
+  AT c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = AT{0, 0, 0, 0};
+  long long t0 = 0, r0 = 0;
+  if (threadIdx.x == 0) {
+    t0 = (long long)__builtin_amdgcn_s_memtime();
+    r0 = wall_clock64();
+  }
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = mma(a, b, c[i]);
+  }
+  if (threadIdx.x == 0) {
+    const long long t1 = (long long)__builtin_amdgcn_s_memtime(), r1 = wall_clock64();
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += (float)c[i][0] + (float)c[i][3];
+  if (s == 1234.5f) out[blockIdx.x] = 1u;
+}
+
+// Streaming read of n 16-byte words, `passes` times over (grid-stride,
+// coalesced, 8 loads in flight per lane).
+__global__ __launch_bounds__(256) void rf_stream_kernel(const int4* __restrict__ p, long long n, int passes,
+                                                        unsigned* out) {
+  int4 acc = make_int4(0, 0, 0, 0);
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (int pass = 0; pass < passes; ++pass) {
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 7 * stride < n; i += 8 * stride) {
+      int4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = p[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x ^= x[u].x;
+        acc.y ^= x[u].y;
+        acc.z ^= x[u].z;
+        acc.w ^= x[u].w;
+      }
+    }
+    for (; i < n; i += stride) {
+      const int4 x = p[i];
+      acc.x ^= x.x;
+      acc.y ^= x.y;
+      acc.z ^= x.z;
+      acc.w ^= x.w;
+    }
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x13572468) out[blockIdx.x] = 1u;
+}
+
+// Rounds of one cross-workgroup selection with nothing else in between,
+// one wave per workgroup, one workgroup per CU.  variant 0: the walk's
+// two-level all-gather with the first level inside an XCD; 1: the same at
+// device scope; 2: a flat all-gather (every workgroup stores its key in 8
+// per-XCD copies and polls all G keys of its copy); 3: Fig. 8 as drawn, a
+// device-scope atomic maximum on one slot and an arrival counter.  Thread 0
+// of each workgroup records the wall clock around the rounds; every
+// workgroup checks that it saw the true maximum (wrong[g] counts misses,
+// timed_out[g] counts expired waits).
+__device__ __forceinline__ unsigned long long rf_key(int g, int r) {
+  // distinct keys with a step-dependent winner, below the step tag
+  const uint32_t h = (uint32_t)(g * 2654435761u) ^ (uint32_t)(r * 40503u);
+  return ((unsigned long long)(h & 0xFFFFFu) << 18) | (unsigned long long)(0x3FFFFu - (uint32_t)g);
+}
+
+__global__ __launch_bounds__(64) void rf_exchange_kernel(int variant, int rounds, Ctrl* ctrl,
+                                                         unsigned long long* flat, unsigned* cnt,
+                                                         long long timeout, long long* clk, unsigned* wrong) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x, G = gridDim.x;
+  long long r0 = 0;
+  if (lane == 0) r0 = wall_clock64();
+  unsigned bad = 0, expired = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const unsigned long long key = rf_key(g, r);
+    unsigned long long want_key = 0ull;
+    for (int q = lane; q < G; q += 64) want_key = umax64(want_key, rf_key(q, r));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 1));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 2));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 4));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 8));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 16));
+    want_key = umax64(want_key, shfl_xor_u64(want_key, 32));
+    unsigned long long win = 0ull;
+    bool ok = true;
+    if (variant <= 1) {
+      ok = exchange<1, false>(ctrl, 0, r, 1, key, timeout, &win, lds, variant == 0);
+      win = __shfl(win, 0, 64);
+    } else if (variant >= 4) {
+      ok = exchange<1, false, true>(ctrl, 0, r, 1, key, timeout, &win, lds, variant == 4);
+      win = __shfl(win, 0, 64);
+    } else if (variant == 2) {
+      const unsigned long long tag = (unsigned long long)(r + 1) << kTagShift;
+      unsigned long long* F = flat + (size_t)(r & 1) * kCopies * kMaxGrid;
+      if (lane < kCopies) st_agent(&F[lane * kMaxGrid + g], tag | key);
+      const long long t0 = wall_clock64();
+      while (true) {
+        bool here = true;
+        unsigned long long best = 0ull;
+        for (int q = lane; q < G; q += 64) {
+          const unsigned long long v = ld_agent(&F[(g % kCopies) * kMaxGrid + q]);
+          here = here && (v >> kTagShift) == (unsigned long long)(r + 1);
+          best = umax64(best, v & kKeyMask);
+        }
+        if (__all(here)) {
+          best = umax64(best, shfl_xor_u64(best, 1));
+          best = umax64(best, shfl_xor_u64(best, 2));
+          best = umax64(best, shfl_xor_u64(best, 4));
+          best = umax64(best, shfl_xor_u64(best, 8));
+          best = umax64(best, shfl_xor_u64(best, 16));
+          best = umax64(best, shfl_xor_u64(best, 32));
+          win = best;
+          break;
+        }
+        if (wall_clock64() - t0 > timeout) {
+          ok = false;
+          break;
+        }
+      }
+    } else {
+      unsigned long long* slot = flat + r;
+      unsigned* c = cnt + r;
+      if (lane == 0) {
+        __hip_atomic_fetch_max(slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const long long t0 = wall_clock64();
+        while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)G) {
+          if (wall_clock64() - t0 > timeout) {
+            ok = false;
+            break;
+          }
+        }
+        win = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      win = __shfl(win, 0, 64);
+      ok = __shfl((int)ok, 0, 64) != 0;
+    }
+    if (!ok) ++expired;
+    else if ((win & kKeyMask) != want_key) ++bad;
+    if (!ok) break;
+  }
+  if (lane == 0) {
+    clk[g] = wall_clock64() - r0;
+    wrong[2 * g] = bad;
+    wrong[2 * g + 1] = expired;
+  }
+}
+
+// One-way latency between workgroup 0 and workgroup `peer`: they pass a
+// counter back and forth `rounds` times.  xcd: plain store and NT poll
+// through the shared L2 (both on one XCD); otherwise device scope.
+__global__ __launch_bounds__(64) void rf_pingpong_kernel(int peer, int xcd, int rounds, unsigned long long* flag,
+                                                         long long timeout, long long* clk) {
+  const int g = blockIdx.x;
+  if ((g != 0 && g != peer) || threadIdx.x != 0) return;
+  const bool first = g == 0;
+  const long long r0 = wall_clock64();
+  unsigned long long* mine = flag + (first ? 0 : 16);
+  const unsigned long long* other = flag + (first ? 16 : 0);
+  long long t0 = r0;
+  bool ok = true;
+  for (int r = 0; r < rounds && ok; ++r) {
+    if (first) {
+      if (xcd) st_xcd(mine, (unsigned long long)r + 1); else st_agent(mine, (unsigned long long)r + 1);
+    }
+    while (true) {
+      unsigned long long v;
+      if (xcd) {
+        const unsigned long long* pp[1] = {other};
+        unsigned long long vv[1];
+        ld_xcd<1>(pp, vv);
+        v = vv[0];
+      } else {
+        v = ld_agent(other);
+      }
+      if (v == (unsigned long long)r + 1) break;
+      if (wall_clock64() - t0 > timeout) {
+        ok = false;
+        break;
+      }
+    }
+    if (!first) {
+      if (xcd) st_xcd(mine, (unsigned long long)r + 1); else st_agent(mine, (unsigned long long)r + 1);
+    }
+    t0 = wall_clock64();
+  }
+  clk[first ? 0 : 1] = ok ? wall_clock64() - r0 : -1;
+}
+
+// VALU issue: n dependent v_add_f32 per lane (one chain), or the same number
+// spread over four independent chains; s_memtime cycles per instruction, one
+// entry per wave (waves w and w + 4 of a workgroup share a SIMD).
+template <bool DEP>
+__global__ __launch_bounds__(1024) void rf_valu_kernel(int n, float seed, float* out, long long* clk) {
+  float a0 = seed + threadIdx.x, a1 = a0 * 0.5f, a2 = a0 * 0.25f, a3 = a0 * 0.125f;
+  const float d = seed * 1e-7f;
+  const long long t0 = (long long)__builtin_amdgcn_s_memtime();
+  for (int i = 0; i < n; i += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (DEP) {
+        a0 = a0 + d;
+        a0 = a0 + d;
+        a0 = a0 + d;
+        a0 = a0 + d;
+      } else {
+        a0 = a0 + d;
+        a1 = a1 + d;
+        a2 = a2 + d;
+        a3 = a3 + d;
+      }
+      asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    }
+  }
+  const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+  if ((threadIdx.x & 63) == 0) clk[threadIdx.x >> 6] = t1 - t0;
+  out[threadIdx.x] = a0 + a1 + a2 + a3;
+}
+
+hipError_t launch_rf_lds(int grid, int rounds, unsigned* out, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute((const void*)rf_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           96 * 1024);
+  if (e != hipSuccess) return e;
+  rf_lds_kernel<<<grid, 512, 96 * 1024, s>>>(rounds, out);
+  return hipGetLastError();
+}
+hipError_t launch_rf_mfma(int wtype, int grid, int rounds, unsigned* out, long long* clk, hipStream_t s) {
+  if (wtype == 0) rf_mfma_kernel<0><<<grid, 512, 0, s>>>(rounds, out, clk);
+  else rf_mfma_kernel<1><<<grid, 512, 0, s>>>(rounds, out, clk);
+  return hipGetLastError();
+}
+hipError_t launch_rf_stream(const void* p, long long n16, int passes, int grid, unsigned* out, hipStream_t s) {
+  rf_stream_kernel<<<grid, 256, 0, s>>>((const int4*)p, n16, passes, out);
+  return hipGetLastError();
+}
+hipError_t launch_rf_exchange(int variant, int grid, int rounds, Ctrl* ctrl, unsigned long long* flat, unsigned* cnt,
+                              long long timeout, long long* clk, unsigned* wrong, hipStream_t s) {
+  const hipError_t e = hipFuncSetAttribute((const void*)rf_exchange_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (e != hipSuccess) return e;
+  // more than half the LDS per workgroup: one workgroup per CU, as in the walk
+  rf_exchange_kernel<<<grid, 64, 96 * 1024, s>>>(variant, rounds, ctrl, flat, cnt, timeout, clk, wrong);
+  return hipGetLastError();
+}
+hipError_t launch_rf_pingpong(int grid, int peer, int xcd, int rounds, unsigned long long* flag, long long timeout,
+                              long long* clk, hipStream_t s) {
+  rf_pingpong_kernel<<<grid, 64, 0, s>>>(peer, xcd, rounds, flag, timeout, clk);
+  return hipGetLastError();
+}
+hipError_t launch_rf_valu(bool dep, int waves, int n, float* out, long long* clk, hipStream_t s) {
+  if (dep) rf_valu_kernel<true><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
+  else rf_valu_kernel<false><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
+  return hipGetLastError();
 }
 
 }  // namespace wts

@@ -33,7 +33,6 @@ struct wts_ctx {
   const float* c = nullptr;
   Ctrl* ctrl = nullptr;
   float* lse_part = nullptr;  // (max, sum) pairs of every workgroup, per row and step
-  unsigned long long walks = 0;
   long long timeout_ticks = 0;
 };
 
@@ -52,7 +51,6 @@ namespace {
 constexpr int kMaxDevices = 64;
 struct DevScratch {
   char* ptr = nullptr;            // device address of `scratch` on that GPU
-  unsigned long long walks = 0;   // walks run on it (their parity alternates)
 };
 DevScratch g_scratch[kMaxDevices];
 std::mutex g_scratch_mu;
@@ -205,27 +203,24 @@ wts_status scratch_init(int device) {
   if (launch_fill_zero(ptr, kNoAllocBytes, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return WTS_ERR_DEVICE;
   g_scratch[device].ptr = (char*)ptr;
-  g_scratch[device].walks = 0;
   return WTS_OK;
 }
 
 // Reads (and with clear resets) the error word of one control block.
-wts_status read_ctrl_error(Ctrl* ctrl, bool clear, unsigned long long* walks) {
+wts_status read_ctrl_error(Ctrl* ctrl, bool clear) {
   unsigned err = 0;
   if (hipMemcpy(&err, &ctrl->err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return WTS_ERR_DEVICE;
   if (clear && err) {
     // A failed walk can leave its slots and counters in any state: start over.
     if (hipMemset(ctrl, 0, sizeof(Ctrl)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
       return WTS_ERR_DEVICE;
-    *walks = 0;
   }
   return (wts_status)err;
 }
 
 // One walk with the given control block and log-normaliser partials
 // (lse_cap bytes of room; the context's own, or the device scratch).
-wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap,
-                     unsigned long long* walks);
+wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap);
 
 }  // namespace
 
@@ -360,23 +355,21 @@ wts_status wts_get_plan(const wts_ctx* ctx, int32_t B, int32_t exec, int32_t tem
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p) {
   if (!ctx || !p) return WTS_ERR_INVALID_ARG;
   const size_t groups = (size_t)std::max(ctx->grid, step_grid(ctx));
-  return walk_impl(ctx, p, ctx->ctrl, ctx->lse_part, (size_t)ctx->max_batch * ctx->max_steps * groups * 8,
-                   &ctx->walks);
+  return walk_impl(ctx, p, ctx->ctrl, ctx->lse_part, (size_t)ctx->max_batch * ctx->max_steps * groups * 8);
 }
 
 wts_status wts_walk_noalloc(wts_ctx* ctx, const wts_walk_params* p) {
   if (!ctx || !p) return WTS_ERR_INVALID_ARG;
   DevScratch& ds = g_scratch[ctx->device];   // set up by wts_create on this device
   if (!ds.ptr) return WTS_ERR_DEVICE;
-  return walk_impl(ctx, p, (Ctrl*)ds.ptr, (float*)(ds.ptr + kNoAllocCtrlBytes), kNoAllocLseBytes, &ds.walks);
+  return walk_impl(ctx, p, (Ctrl*)ds.ptr, (float*)(ds.ptr + kNoAllocCtrlBytes), kNoAllocLseBytes);
 }
 
 }  // extern "C"
 
 namespace {
 
-wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap,
-                     unsigned long long* walks) {
+wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap) {
   if (p->B < 1 || p->B > ctx->max_batch || p->gamma < 1 || p->gamma > ctx->max_steps) return WTS_ERR_INVALID_ARG;
   if (p->temperature != 0 && p->temperature != 1) return WTS_ERR_INVALID_ARG;
   if (p->step_offset < 0 || (p->flags & ~WTS_WALK_FIXED_LATENT) != 0) return WTS_ERR_INVALID_ARG;
@@ -425,7 +418,6 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   a.temperature = p->temperature;
   a.seed_lo = (unsigned)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (unsigned)(p->seed >> 32);
-  a.parity = (int)(*walks & 1ull);
   a.base = p->base;
   a.x0 = p->x0;
   a.h0 = p->h0;
@@ -456,7 +448,6 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
     if (e == hipSuccess && a.lse) e = launch_lse(a, ctx->grid, s);
   }
   if (e != hipSuccess) return WTS_ERR_DEVICE;
-  ++*walks;
   return WTS_OK;
 }
 
@@ -468,11 +459,11 @@ wts_status wts_get_error(wts_ctx* ctx, int clear) {
   if (!ctx) return WTS_ERR_INVALID_ARG;
   DeviceGuard guard(ctx->device);
   if (hipDeviceSynchronize() != hipSuccess) return WTS_ERR_DEVICE;
-  wts_status st = read_ctrl_error(ctx->ctrl, clear != 0, &ctx->walks);
+  wts_status st = read_ctrl_error(ctx->ctrl, clear != 0);
   // walks through wts_walk_noalloc latch into the device scratch
   DevScratch& ds = g_scratch[ctx->device];
   if (ds.ptr) {
-    const wts_status s2 = read_ctrl_error((Ctrl*)ds.ptr, clear != 0, &ds.walks);
+    const wts_status s2 = read_ctrl_error((Ctrl*)ds.ptr, clear != 0);
     if (st == WTS_OK) st = s2;
   }
   return st;

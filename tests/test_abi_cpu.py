@@ -10,10 +10,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wts.h")
+ROOFLINE_HEADER = os.path.join(ROOT, "include", "wts_roofline.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(wts_[a-z_]+)\s*\(", text)))
 
@@ -23,13 +24,19 @@ def test_header_declares_expected_entry_points():
     assert set(_declared_functions()) == set(_abi.EXPORTS)
 
 
+def test_roofline_header_declares_its_entry_point():
+    from serial_draft_head_persistent_amd import _abi
+    assert set(_declared_functions(ROOFLINE_HEADER)) == set(_abi.ROOFLINE_EXPORTS)
+
+
 def test_library_exports_every_declared_symbol():
     from serial_draft_head_persistent_amd import _abi
     lib = _abi.load()
-    for name in _declared_functions():
+    names = _declared_functions() + _declared_functions(ROOFLINE_HEADER)
+    for name in names:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
-    for name in _declared_functions():
+    for name in names:
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
 
 
@@ -42,12 +49,14 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("cname,pyname", [("wts_create_params", "CreateParams"),
-                                          ("wts_walk_params", "WalkParams"), ("wts_plan", "Plan")])
+                                          ("wts_walk_params", "WalkParams"), ("wts_plan", "Plan"),
+                                          ("wts_roofline_result", "RooflineResult")])
 def test_struct_layout_matches_c(cname, pyname):
     from serial_draft_head_persistent_amd import _abi
     st = getattr(_abi, pyname)
     fields = [f for f, _ in st._fields_]
-    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "wts.h"', 'int main(void) {',
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "wts.h"', '#include "wts_roofline.h"',
+           'int main(void) {',
            f'  printf("%zu\\n", sizeof({cname}));']
     src += [f'  printf("%zu\\n", offsetof({cname}, {f}));' for f in fields]
     src += ['  return 0;', '}']
@@ -114,3 +123,6 @@ def test_null_context_and_params_are_rejected():
     plan = _abi.Plan()
     assert lib.wts_get_plan(None, 1, 0, 0, ctypes.byref(plan)) == 1
     lib.wts_destroy(None)  # a no-op
+    assert lib.wts_roofline(0, None) == 1
+    r = _abi.RooflineResult()
+    assert lib.wts_roofline(-1, ctypes.byref(r)) == 1
