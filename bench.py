@@ -13,6 +13,12 @@ cores, and side measurements (batch and temperature sweep, bf16 248k,
 recurrent head, fused-streaming and step-wise execution).
 
     python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu]
+    python bench.py --profile-walk NAME   (one workload's walks only, for rocprofv3)
+
+Roofline denominators are measured on the same device by wts_roofline()
+(LDS and MFMA operand rates, shader clock, HBM and memory-side-cache stream
+rates, the cross-workgroup selection round in isolation, VALU issue rate);
+the published peaks are reported beside them.
 """
 import argparse
 import json
@@ -30,6 +36,16 @@ I8_PEAK_TOPS = 5000.0          # dense int8 MFMA, published (TOP/s)
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
 
 
+# Workloads whose walks --profile-walk runs alone (name: (config, B, gamma,
+# T, create kwargs)), for rocprofv3 kernel traces and counter passes.
+PROFILE_WALKS = {
+    "markov-int8-v151936-b1-g16": (1, 1, 16, 0, {}),
+    "markov-bf16-v248320-b16-g16": (3, 16, 16, 0, {}),
+    "markov-int8-v151936-b16-g16-partial": (2, 16, 16, 0, {"resident_tiles": 2, "lds_tiles": 0}),
+    "markov-int8-v151936-b16-g16-t1": (2, 16, 16, 1, {}),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,6 +61,8 @@ def parse():
     ap.add_argument("--summarize-counters", metavar="CSV",
                     help="print the per-dispatch mean of every counter in a rocprofv3 --pmc "
                          "counter_collection.csv for the headline kernel, and exit")
+    ap.add_argument("--profile-walk", choices=sorted(PROFILE_WALKS),
+                    help="run only the timed walks of one workload (for rocprofv3 runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --profile: also run a plain 512 MiB device copy (known bytes) so a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE")
@@ -108,43 +126,111 @@ def cold_walks(head, t, n, flush_bytes=512 << 20, **kw):
     return np.array(us)
 
 
-CLOCK_GHZ = 2.4          # MI355X peak engine clock
 SIMDS_PER_CU = 4
-MFMA_CYCLES = 16         # v_mfma_i32_16x16x64_i8 and v_mfma_f32_16x16x32_bf16: 32,768 and
-                         # 16,384 ops per SIMD in 16 cycles, i.e. the published dense peaks
+MFMA_OPS_I8 = 16 * 16 * 64 * 2     # one v_mfma_i32_16x16x64_i8
+MFMA_B_BYTES = 64 * 16             # its B operand: 64 lanes x 16 bytes of W
+# VALU instructions per Gumbel value of the T=1 noise: the noise loop of
+# walk_kernel<0, 16, 0, 1, false, false> issues 338 VALU instructions per
+# Philox4x32-10 call, which yields four values (one counter, four words).
+NOISE_VALU_PER_VALUE = 338 / 4
 
 
-def step_rooflines(plan, V, r, B, fit):
-    """Rooflines of the resident step and of the entry (int8 W, Markov, B rows).
+def step_rooflines(plan, V, r, B, fit, rf):
+    """Rooflines of the resident step (int8 W, Markov, B rows), against the
+    denominators measured on this device (rf = wts_roofline()).
 
-    Resident step: every W tile is an MFMA B operand read from registers or
-    LDS; the step cannot end before the busiest SIMD has issued the MFMAs of
-    its tiles (r/64 int8 MFMAs per tile, 16 cycles each).  At B=1 only the
-    hi/lo pair of rows in each MFMA's A block is distinct, so the useful int8
-    ops (2 vectors x 2 ops per MAC x V x r per batch row) are a small part of
-    the MFMA peak.  Entry: the shard's one-time load from HBM."""
+    Resident step, per SIMD: every W tile is an MFMA B operand read from
+    registers or LDS; the busiest SIMD issues r/64 int8 MFMAs per tile of its
+    share, at the measured MFMA rate.  On-chip operand rate, aggregate: the W
+    bytes of one step against the measured rate at which all CUs' MFMAs take
+    B operands (1 KiB per MFMA) and LDS delivers reads (the north-star's
+    resident-bandwidth roofline).  Step floor: that bound plus one
+    cross-workgroup selection round measured in isolation.  Entry: the shard's
+    one-time load against the measured HBM rate."""
+    G = rf["grid"]
     tiles_cu = -(-plan["tiles"] // plan["grid"])
     tiles_simd = -(-tiles_cu // SIMDS_PER_CU)
     mfma_simd = tiles_simd * (r // 64)
-    bound_us = mfma_simd * MFMA_CYCLES / (CLOCK_GHZ * 1e3)
+    mfma_rate_simd = rf["mfma_i8_TOPs"] * 1e12 / MFMA_OPS_I8 / (G * SIMDS_PER_CU)   # MFMA/s per SIMD
+    bound_us = mfma_simd / mfma_rate_simd * 1e6
     slope, entry = fit["per_step_us"], max(fit["entry_us"], 1e-3)
+    w_bytes = V * r
+    w_lds = plan["lds_tiles"] * plan["waves"] * plan["grid"] * 16 * r
+    w_reg = max(0, min(plan["resident_bytes"], w_bytes) - w_lds)
+    operand_GBps = rf["mfma_i8_TOPs"] * 1e12 / MFMA_OPS_I8 * MFMA_B_BYTES / 1e9
+    onchip_us = (w_reg / (operand_GBps * 1e9) + w_lds / (rf["lds_read_GBps"] * 1e9)) * 1e6
+    floor_us = bound_us + rf["exchange_us"][0]
     useful_ops = 2.0 * 2 * V * r * B
     return {
         "resident_step_roofline": {
-            "bound": "mfma issue, W operands on chip", "tiles_per_cu": tiles_cu,
-            "mfma_per_simd_per_step": mfma_simd, "bound_us": round(bound_us, 3),
-            "onchip_w_read_TBps_at_bound": round(V * r / (bound_us * 1e-6) / 1e12, 1),
-            "onchip_w_read_TBps": round(V * r / (slope * 1e-6) / 1e12, 1),
-            "frac": round(bound_us / slope, 4)},
+            "bound": "mfma issue on the busiest SIMD, W operands on chip (measured MFMA rate)",
+            "tiles_per_cu": tiles_cu, "mfma_per_simd_per_step": mfma_simd,
+            "mfma_cycles_measured": round(rf["clock_MHz"] * 1e6 / mfma_rate_simd, 2),
+            "bound_us": round(bound_us, 3), "frac": round(bound_us / slope, 4)},
+        "onchip_operand_roofline": {
+            "bound": "aggregate on-chip operand rate (MFMA B operands from registers, LDS reads), measured",
+            "register_w_bytes": int(w_reg), "lds_w_bytes": int(w_lds),
+            "operand_rate_GBps": round(operand_GBps, 0), "lds_read_GBps": round(rf["lds_read_GBps"], 0),
+            "achieved_GBps": round(w_bytes / (slope * 1e-6) / 1e9, 0),
+            "bound_us": round(onchip_us, 3), "frac": round(onchip_us / slope, 4)},
+        "step_floor": {
+            "bound": "resident-step bound + one selection round in isolation (both measured)",
+            "exchange_round_us": round(rf["exchange_us"][0], 3), "floor_us": round(floor_us, 3),
+            "frac": round(floor_us / slope, 4)},
         "useful_int8_ops": {"ops_per_step": int(useful_ops),
                             "achieved_TOPs": round(useful_ops / (slope * 1e-6) / 1e12, 1),
-                            "peak_TOPs": I8_PEAK_TOPS,
-                            "frac": round(useful_ops / (slope * 1e-6) / 1e12 / I8_PEAK_TOPS, 4)},
+                            "peak_TOPs_published": I8_PEAK_TOPS, "peak_TOPs_measured": round(rf["mfma_i8_TOPs"], 0),
+                            "frac_measured": round(useful_ops / (slope * 1e-6) / 1e12 / rf["mfma_i8_TOPs"], 4)},
         "entry_roofline": {"bound": "hbm", "bytes": int(V * r + 4 * V),
                            "achieved_GBps": round((V * r + 4 * V) / (entry * 1e-6) / 1e9, 1),
-                           "peak_GBps": HBM_PEAK_GBS,
-                           "frac": round((V * r + 4 * V) / (entry * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                           "peak_GBps_published": HBM_PEAK_GBS, "peak_GBps_measured": round(rf["hbm_read_GBps"], 0),
+                           "frac_measured": round((V * r + 4 * V) / (entry * 1e-6) / 1e9 / rf["hbm_read_GBps"], 4)},
     }
+
+
+def graph_walks(head, t, n, **kw):
+    """Per-walk times (us) of one walk captured in a HIP graph and replayed n times."""
+    import torch
+    out = head.walk(t["base"], t["x0"], h0=t.get("h0"), **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        head.walk(t["base"], t["x0"], h0=t.get("h0"), out=out, **kw)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    err = head.error()
+    if err != "WTS_OK":
+        raise RuntimeError(err)
+    del g
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def _stream_report(fit, plan, rf):
+    """Per-step streamed W bytes against the measured stream rates (HBM, and a
+    128 MiB working set in the memory-side cache)."""
+    slope = fit["per_step_us"]
+    gbps = plan["streamed_bytes"] / (slope * 1e-6) / 1e9
+    return {"per_step_us": round(slope, 3), "entry_us": round(fit["entry_us"], 2),
+            "median_us_g16": round(fit["median_us"][-1], 2),
+            "streamed_MB_per_step": round(plan["streamed_bytes"] / 1e6, 2),
+            "resident_MB": round(plan["resident_bytes"] / 1e6, 1),
+            "stream_GBps": round(gbps, 1),
+            "frac_of_hbm_measured": round(gbps / rf["hbm_read_GBps"], 4),
+            "frac_of_mall_measured": round(gbps / rf["mall_read_GBps"], 4)}
 
 
 def walk_stats(us):
@@ -152,14 +238,14 @@ def walk_stats(us):
             "p90_us": float(np.percentile(us, 90))}
 
 
-def fit_steps(head, d, t, gammas=(1, 7, 16), n=100, warmup=10, **kw):
-    """Least-squares line over complete walks of gamma steps: slope = per-step cost, intercept = entry."""
-    import torch
+def fit_steps(head, d, t, gammas=(1, 7, 16), n=100, warmup=10, graph=False, **kw):
+    """Least-squares line over complete walks of gamma steps: slope = per-step cost, intercept = entry.
+    graph: each walk captured in a HIP graph and replayed."""
     med = []
     for g in gammas:
         tg = dict(t)
         tg["base"] = t["base"][:, :g].contiguous()
-        _, us = timed_walks(head, tg, n, warmup, **kw)
+        us = graph_walks(head, tg, n, **kw) if graph else timed_walks(head, tg, n, warmup, **kw)[1]
         med.append(float(np.median(us)))
     A = np.vstack([np.array(gammas, float), np.ones(len(gammas))]).T
     slope, icpt = np.linalg.lstsq(A, np.array(med), rcond=None)[0]
@@ -272,9 +358,20 @@ def cpu_baseline(d, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or walks >= 400:
             break
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": el / walks * 1e6, "unit": "us/walk", "cores": int(threads), "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "cpu_model": model, "blas_threads": int(threads),
             "sample": f"{walks} complete walks of the headline workload (V=151936, B=1, gamma=16, greedy), "
-                      f"{el:.1f} s; int8 dot products via fp64 BLAS, epilogue single-threaded numpy"}
+                      f"{el:.1f} s; int8 dot products via fp64 BLAS on {threads} threads, epilogue "
+                      f"single-threaded numpy"}
 
 
 def main():
@@ -296,6 +393,19 @@ def main():
 
     dev_name = torch.cuda.get_device_name(0)
     log("device", dev_name)
+    if args.profile_walk:
+        cfg, B_, g_, T_, ckw = PROFILE_WALKS[args.profile_walk]
+        dp = datagen.config_inputs(cfg, B=B_, gamma=g_)
+        hp, tp = make_head(dp, **ckw)
+        log("plan", hp.plan(B_, temperature=T_))
+        m, u = timed_walks(hp, tp, args.steps, args.warmup, temperature=T_)
+        print(json.dumps({"workload": args.profile_walk, "us_per_walk": m * 1e3,
+                          "median_us": float(np.median(u)), "walks": args.steps}))
+        hp.close()
+        return
+    import serial_draft_head_persistent_amd as wts
+    rf = wts.roofline(0)
+    log("measured denominators", rf)
     t_gen = time.perf_counter()
     d = datagen.config_inputs(1)
     t = dev_inputs(d)
@@ -332,6 +442,8 @@ def main():
     traffic = committed_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "peak_measured": round(rf["hbm_read_GBps"], 1),
+                "frac_measured": round(achieved / rf["hbm_read_GBps"], 4),
                 "traffic": None if traffic is None else round(traffic / (ms_per_walk * 1e-3) / 1e9, 1),
                 "algorithmic_bytes_per_launch": int(hbm_bytes),
                 "traffic_bytes_per_launch": None if traffic is None else int(traffic)}
@@ -340,10 +452,10 @@ def main():
         "w_read_GBps_per_step": round(w_bytes / (fit["per_step_us"] * 1e-6) / 1e9, 1),
         "entry_w_load_GBps": round(w_bytes / (max(fit["entry_us"], 1e-3) * 1e-6) / 1e9, 1),
     }
-    per_step.update(step_rooflines(plan, V, r, B, fit))
+    per_step.update(step_rooflines(plan, V, r, B, fit, rf))
     log("per-step rooflines", per_step)
 
-    extras = {"walk": walk_stats(us), "fit_resident": fit, "plan": plan}
+    extras = {"walk": walk_stats(us), "fit_resident": fit, "plan": plan, "measured_denominators": rf}
     extras["walk_cold_cache"] = walk_stats(cold_walks(head, t, 50))
     log("cold-cache walks", extras["walk_cold_cache"])
     extras["breakdown_resident"] = breakdown(head, t)
@@ -354,8 +466,13 @@ def main():
         for ex in ("stream", "stepwise"):
             extras[f"fit_{ex}"] = fit_steps(head, d, t, exec=ex)
             log(ex, extras[f"fit_{ex}"])
-        # Fig. 13b analog: the fixed-latent probe repeats projection and selection
-        # with the latent of step 0; the difference of the slopes is the state advance
+        # Fig. 3b / Fig. 11: the step-wise baseline and the resident walk captured
+        # once in a HIP graph and replayed (no launch gaps from the host)
+        for ex in ("stepwise", "resident"):
+            extras[f"fit_{ex}_graph"] = fit_steps(head, d, t, exec=ex, graph=True)
+            log(ex, "graph", extras[f"fit_{ex}_graph"])
+        # Fig. 13b analogue: walks with the step-0 latent held fixed; the
+        # slope difference is what advancing the state costs per step
         fx = fit_steps(head, d, t, fixed_latent=True)
         extras["fit_fixed_latent"] = fx
         extras["advance_us_per_step"] = round(fit["per_step_us"] - fx["per_step_us"], 3)
@@ -396,8 +513,36 @@ def main():
                                                      for k in ("reg_tiles", "lds_tiles", "stream_tiles")]})
             log("sweep B", B_, sweep[-2:])
         extras["sweep_markov_int8_v151936"] = sweep
+        # T=1 Gumbel noise against its VALU bound: B x V values per step, each
+        # NOISE_VALU_PER_VALUE wave64 instructions (64 values per instruction),
+        # spread over every SIMD at the measured four-waves-per-SIMD issue rate
+        noise = []
+        for B_ in (1, 2, 4, 8, 16):
+            m0 = next(x["median_us"] for x in sweep if x["B"] == B_ and x["T"] == 0)
+            m1 = next(x["median_us"] for x in sweep if x["B"] == B_ and x["T"] == 1)
+            instr = B_ * V * NOISE_VALU_PER_VALUE / 64
+            cyc_simd = instr / (rf["grid"] * SIMDS_PER_CU) * rf["valu_indep_4w_cycles"] / 4
+            bound_step = cyc_simd / rf["clock_MHz"]
+            bound_walk = m0 + 16 * bound_step
+            noise.append({"B": B_, "noise_valu_bound_us_per_step": round(bound_step, 3),
+                          "noise_measured_us_per_step": round((m1 - m0) / 16, 3),
+                          "greedy_plus_bound_us": round(bound_walk, 1), "t1_walk_us": m1,
+                          "t1_over_bound": round(m1 / bound_walk, 3)})
+        extras["noise_roofline_t1"] = noise
+        log("noise roofline", noise)
+        # streamed tiles (partial residency), int8: two register tiles per wave,
+        # the rest streamed every step
+        hp, _ = make_head(d, t, resident_tiles=2, lds_tiles=0)
+        d16 = datagen.config_inputs(1, B=16, gamma=16, seed=1)
+        t16 = {"base": torch.from_numpy(d16["base"].view(np.int16)).view(torch.bfloat16).cuda(),
+               "x0": torch.from_numpy(d16["x0"]).cuda()}
+        pp = hp.plan(16)
+        fp = fit_steps(hp, d16, t16, n=50, warmup=5)
+        extras["stream_int8_v151936_b16_partial"] = _stream_report(fp, pp, rf)
+        log("stream int8 partial", extras["stream_int8_v151936_b16_partial"])
+        hp.close()
         head.close()
-        del t
+        del t, t16
         torch.cuda.empty_cache()
         # bf16 W, V = 248,320 (partial residency)
         d3 = datagen.config_inputs(3, B=16, gamma=16)
@@ -412,6 +557,10 @@ def main():
                        "streamed_MB_per_step": round(p3["streamed_bytes"] / 1e6, 1)})
         extras["markov_bf16_v248320"] = r3
         log("bf16 248k", r3)
+        # the partially resident sixteen-row walk against the stream rates
+        f3 = fit_steps(h3, d3, t3, n=50, warmup=5)
+        extras["stream_bf16_v248320_b16"] = _stream_report(f3, h3.plan(16), rf)
+        log("stream bf16 248k B=16", extras["stream_bf16_v248320_b16"])
         h3.close()
         del t3, d3
         torch.cuda.empty_cache()

@@ -398,16 +398,11 @@ struct Roles {
 
 // ---- workgroup-local selection keys ----
 // Inside a workgroup a key orders (score, -row) with the row counted from the
-// workgroup's first vocabulary row: T=0 uses 32 bits (16-bit order of the
-// bf16 logit, 16-bit row), T=1 64 bits (32-bit order of the fp32 score).
-// 0 means "no candidate".  -0 is folded into +0.
+// workgroup's first vocabulary row: T=0 uses 32 bits (a 16-bit order code of
+// the bf16 logit, 16-bit row), T=1 64 bits (32-bit order of the fp32 score).
+// 0 means "no candidate".  -0 ranks equal to +0.
 template <int TEMP> struct LKey { typedef uint32_t T; };
 template <> struct LKey<1> { typedef unsigned long long T; };
-
-__device__ __forceinline__ uint32_t ord16(uint32_t h) {
-  h = (h == 0x8000u) ? 0u : h;
-  return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
-}
 __device__ __forceinline__ uint32_t ord32(uint32_t b) {
   b = (b == 0x80000000u) ? 0u : b;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -415,12 +410,13 @@ __device__ __forceinline__ uint32_t ord32(uint32_t b) {
 __device__ __forceinline__ uint32_t kmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
-// Workgroup-local key -> device-wide key (same layout as sel_key: order of
-// the fp32 score in bits 49..18, 0x3FFFF - v in bits 17..0).
+// Workgroup-local key -> device-wide key (same layout as sel_key: an order
+// code of the score in bits 49..18, 0x3FFFF - v in bits 17..0).  T=0 keys of
+// all workgroups come through the same code, so only their ranking matters.
 __device__ __forceinline__ unsigned long long global_key(uint32_t k, int row0) {
   if (k == 0u) return 0ull;
   const uint32_t o16 = k >> 16;
-  const uint32_t o32 = (o16 << 16) | ((o16 & 0x8000u) ? 0u : 0xFFFFu);  // order of the widened bf16
+  const uint32_t o32 = (o16 << 16) | ((o16 & 0x8000u) ? 0u : 0xFFFFu);  // widened, still monotone
   const uint32_t v = (uint32_t)row0 + (0xFFFFu - (k & 0xFFFFu));
   return ((unsigned long long)o32 << 18) | (unsigned long long)(0x3FFFFu - v);
 }
@@ -620,21 +616,29 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
       z = acc[e];
     }
     z = z + bf16_f32(bv[e]);
-    const uint32_t lg = bf16_rne(z);
+    // bf16 rounding to nearest even: the upper half of r is the logit
+    const uint32_t zb = __float_as_uint(z);
+    const uint32_t r = zb + 0x7FFFu + ((zb >> 16) & 1u);
     if (a.logits != nullptr) {  // uniform: skipped entirely when logits are not requested
-      if (okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)lg;
+      if (okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)(r >> 16);
     }
-    ls.add(m, e, bf16_f32(lg), okb);
+    const float lf = __uint_as_float(r & 0xFFFF0000u);  // the logit, widened exactly
+    ls.add(m, e, lf, okb);
     typename LKey<TEMP>::T k;
     if (TEMP == 0) {
-      k = (ord16(lg) << 16) | lrow;
+      // order of the bf16 logit in the upper half: positives above negatives,
+      // negatives complemented and moved up by one so that -0 ties with +0
+      // (the ranking of the rounded logit with -0 taken as +0), row field below
+      const uint32_t sg = (uint32_t)((int32_t)r >> 31);
+      const uint32_t o = (r ^ (sg | 0x80000000u)) + (sg & 0x10000u);
+      k = (o & 0xFFFF0000u) | lrow;
     } else {
       // lanes without a valid pair read the buffer's first element
       // GP: this entry's noise was read from LDS at the start of the step
       const float g = GP   ? gpre[e]
                       : NZ ? noise[okb ? b * a.noise_stride + (v - row0) : 0]
                            : gumbel(a.seed_lo, a.seed_hi, b, a.step_offset + t, v);
-      const float sc = bf16_f32(lg) + g;
+      const float sc = lf + g;
       k = ((unsigned long long)ord32(__float_as_uint(sc)) << 16) | lrow;
     }
     best[m][e] = kmax(best[m][e], okb ? k : (typename LKey<TEMP>::T)0);
