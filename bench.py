@@ -466,6 +466,13 @@ def main():
         for ex in ("stream", "stepwise"):
             extras[f"fit_{ex}"] = fit_steps(head, d, t, exec=ex)
             log(ex, extras[f"fit_{ex}"])
+        # the guaranteed co-residency of a cooperative launch, at its cost
+        hc, _ = make_head(d, t, cooperative=True)
+        _, uc = timed_walks(hc, t, 100, 10)
+        hc.close()
+        extras["cooperative_launch"] = {"median_us": round(float(np.median(uc)), 2),
+                                        "plain_launch_median_us": round(float(np.median(us)), 2)}
+        log("cooperative", extras["cooperative_launch"])
         # Fig. 3b / Fig. 11: the step-wise baseline and the resident walk captured
         # once in a HIP graph and replayed (no launch gaps from the host)
         for ex in ("stepwise", "resident"):
