@@ -62,8 +62,13 @@ enum { WTS_EXEC_RESIDENT = 0, WTS_EXEC_STREAM = 1, WTS_EXEC_STEPWISE = 2 };
  *  FIXED_LATENT: the fixed-latent probe of Fig. 13b.  Every step projects and
  *            selects with the latent of step 0 (Markov: E[x0]; recurrent:
  *            h_1); each step's choice is written to tokens_out but does not
- *            feed back.  It times a step without its state advance. */
-enum { WTS_WALK_FIXED_LATENT = 1 };
+ *            feed back.  It times a step without its state advance.
+ *  STRESS:   persistent executions only: before each step's cross-workgroup
+ *            selection every workgroup waits a pseudo-random time (0 to about
+ *            1 us, from its index, the step and the seed), so that keys arrive
+ *            in orders a normal walk rarely produces.  Results are unchanged;
+ *            for testing the selection (Fig. 8). */
+enum { WTS_WALK_FIXED_LATENT = 1, WTS_WALK_STRESS = 2 };
 
 typedef struct wts_ctx wts_ctx;
 
@@ -133,6 +138,14 @@ typedef struct wts_walk_params {
                              lossless verifier needs, without a second pass
                              over the logits.  Accumulated in fp32 in the
                              kernel (online max and rescaled sum).            */
+  uint64_t* winners_out;  /* device, [gamma][B][grid] uint64, or NULL.
+                             Persistent executions only: the winning selection
+                             key each workgroup observed at each step for each
+                             batch row (bits 49..18 the score's order code,
+                             bits 17..0 0x3FFFF - token).  Every workgroup must
+                             observe the same key: a race check of Fig. 8.
+                             With WTS_EXEC_STEPWISE (or the STRESS flag there)
+                             the walk returns WTS_ERR_UNSUPPORTED.             */
 } wts_walk_params;
 
 typedef struct wts_plan {

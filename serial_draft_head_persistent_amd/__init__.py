@@ -82,7 +82,7 @@ class Head:
 
     def walk(self, base, x0, *, h0=None, temperature=0, seed=0, step_offset=0, logits=False,
              state=False, lse=False, exec="resident", fixed_latent=False, stream=None, out=None,
-             trace=False, noalloc=False):
+             trace=False, noalloc=False, stress=False, winners=False):
         """Enqueue one walk.  base: bf16 [B, gamma, V]; x0: int32 [B].
 
         Returns a dict of output tensors (tokens int32 [B, gamma]; logits bf16
@@ -92,6 +92,9 @@ class Head:
         uses the latent of step 0).  Pass `out` (a dict from an earlier call)
         to reuse its buffers.  noalloc=True runs the walk through
         wts_walk_noalloc (scratch in the library's fixed per-GPU array).
+        stress delays workgroups at random before each selection; winners
+        returns the key each workgroup observed (uint64 as int64 [gamma, B,
+        grid]); both for testing the selection.
         """
         torch = self._torch
         B, gamma, V = base.shape
@@ -106,14 +109,17 @@ class Head:
                                            device=self.device)
             if lse:
                 out["lse"] = torch.empty((B, gamma), dtype=torch.float32, device=self.device)
+            if winners:
+                out["winners"] = torch.zeros((gamma, B, self.plan(B)["grid"]), dtype=torch.int64,
+                                             device=self.device)
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         p = _abi.WalkParams(B=B, gamma=gamma, step_offset=step_offset, temperature=temperature,
                             seed=seed, base=_ptr(base), x0=_ptr(x0), h0=_ptr(h0),
                             tokens_out=_ptr(out["tokens"]), logits_out=_ptr(out.get("logits")),
                             state_out=_ptr(out.get("state")), exec=EXEC[exec],
-                            flags=_abi.WALK_FIXED_LATENT if fixed_latent else 0,
+                            flags=(_abi.WALK_FIXED_LATENT if fixed_latent else 0) | (_abi.WALK_STRESS if stress else 0),
                             stream=ctypes.c_void_p(s.cuda_stream), trace_out=_ptr(out.get("trace")),
-                            lse_out=_ptr(out.get("lse")))
+                            lse_out=_ptr(out.get("lse")), winners_out=_ptr(out.get("winners")))
         if noalloc:
             _check(_abi.lib().wts_walk_noalloc(self._h, ctypes.byref(p)), "wts_walk_noalloc")
         else:

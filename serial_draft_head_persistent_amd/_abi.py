@@ -17,6 +17,7 @@ HEAD = {"markov": 0, "recurrent": 1}
 WTYPE = {"int8": 0, "bf16": 1}
 EXEC = {"resident": 0, "stream": 1, "stepwise": 2}
 WALK_FIXED_LATENT = 1
+WALK_STRESS = 2
 
 EXPORTS = ["wts_create", "wts_walk", "wts_destroy", "wts_get_error", "wts_get_plan", "wts_status_string",
            "wts_check_log_ratio", "wts_walk_noalloc"]
@@ -40,7 +41,7 @@ class WalkParams(ctypes.Structure):
                 ("seed", c_uint64), ("base", c_void_p), ("x0", c_void_p), ("h0", c_void_p),
                 ("tokens_out", c_void_p), ("logits_out", c_void_p), ("state_out", c_void_p),
                 ("exec", c_int32), ("flags", c_int32), ("stream", c_void_p), ("trace_out", c_void_p),
-                ("lse_out", c_void_p)]
+                ("lse_out", c_void_p), ("winners_out", c_void_p)]
 
 
 class Plan(ctypes.Structure):

@@ -130,6 +130,8 @@ struct WalkArgs {
   float* lse;              // [B][gamma] log normaliser per step, or null
   float* lse_part;         // [B][gamma][grid] (max, sum) pairs of the workgroups (scratch)
   int xcd_l1;              // 1: first exchange level inside one XCD's L2; 0: device scope
+  int stress;              // pseudo-random delay of every workgroup before each exchange
+  unsigned long long* winners;  // [gamma][B][grid] winning key each workgroup observed, or null
 };
 
 // Launchers (wts_kernels.hip).  Each returns the HIP error of its launch.

@@ -1751,6 +1751,15 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         for (int ww = 0; ww < NW; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + lane]);
         k = global_key(lk, row0);
       }
+      if (a.stress) {
+        // testing aid: arrive late by a pseudo-random 0..15 x 128 cycles
+        uint32_t h = (uint32_t)g * 0x9E3779B1u ^ (uint32_t)(t + 1) * 0x85EBCA77u ^ a.seed_lo;
+        h ^= h >> 15;
+        h *= 0x2C1B3C6Du;
+        h ^= h >> 13;
+        const int n = __builtin_amdgcn_readfirstlane((int)(h & 15u));
+        for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(2);
+      }
       unsigned long long win;
       const bool ok = exchange<BB, CAND>(ctrl, par, t, a.B, k, a.timeout_ticks, &win, lds, a.xcd_l1 != 0);
       if (!ok && lane == 0) {
@@ -1758,6 +1767,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         *sflag = 1;
       }
       if (lane < a.B) {
+        if (a.winners != nullptr) a.winners[(unsigned)((t * a.B + lane) * G + g)] = win;
         int x = key_token(win);
         if (!ok || x < 0 || x >= a.V) {  // only after a failed exchange; keep every access in bounds
           if (ok) latch_error(ctrl, 5u);

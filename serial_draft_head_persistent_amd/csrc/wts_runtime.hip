@@ -372,15 +372,17 @@ namespace {
 wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* lse_part, size_t lse_cap) {
   if (p->B < 1 || p->B > ctx->max_batch || p->gamma < 1 || p->gamma > ctx->max_steps) return WTS_ERR_INVALID_ARG;
   if (p->temperature != 0 && p->temperature != 1) return WTS_ERR_INVALID_ARG;
-  if (p->step_offset < 0 || (p->flags & ~WTS_WALK_FIXED_LATENT) != 0) return WTS_ERR_INVALID_ARG;
+  if (p->step_offset < 0 || (p->flags & ~(WTS_WALK_FIXED_LATENT | WTS_WALK_STRESS)) != 0) return WTS_ERR_INVALID_ARG;
   if (p->exec < WTS_EXEC_RESIDENT || p->exec > WTS_EXEC_STEPWISE) return WTS_ERR_INVALID_ARG;
   if (!p->base || !p->x0 || !p->tokens_out) return WTS_ERR_INVALID_ARG;
   if (ctx->head == WTS_HEAD_RECURRENT && !p->h0) return WTS_ERR_INVALID_ARG;
   if (((uintptr_t)p->base & 1) || ((uintptr_t)p->x0 & 3) || ((uintptr_t)p->tokens_out & 3) ||
       ((uintptr_t)p->logits_out & 1) || ((uintptr_t)p->h0 & 3) || ((uintptr_t)p->state_out & 3) ||
-      ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3))
+      ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3) || ((uintptr_t)p->winners_out & 7))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
+  // the forced delays and the winner record belong to the persistent kernel's exchange
+  if (p->exec == WTS_EXEC_STEPWISE && ((p->flags & WTS_WALK_STRESS) || p->winners_out)) return WTS_ERR_UNSUPPORTED;
   {
     // room for the (max, sum) pair of every workgroup, row and step
     const size_t groups = (size_t)(p->exec == WTS_EXEC_STEPWISE ? step_grid(ctx) : ctx->grid);
@@ -431,6 +433,8 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   a.lse = p->lse_out;
   a.lse_part = lse_part;
   a.xcd_l1 = ctx->xcd_l1 ? 1 : 0;
+  a.stress = (p->flags & WTS_WALK_STRESS) != 0;
+  a.winners = (unsigned long long*)p->winners_out;
   hipStream_t s = (hipStream_t)p->stream;
 
   hipError_t e;

@@ -32,14 +32,15 @@ def make_head(d, t=None, **kw):
 
 
 def run(head, t, *, base=None, x0=None, h0=None, temperature=0, seed=0, step_offset=0, exec="resident",
-        logits=True, state=None, lse=False, fixed_latent=False):
+        logits=True, state=None, lse=False, fixed_latent=False, stress=False, winners=False):
     import torch
     base = t["base"] if base is None else base
     x0 = t["x0"] if x0 is None else x0
     h0 = t["h0"] if h0 is None else h0
     state = (head.head == "recurrent") if state is None else state
     o = head.walk(base, x0, h0=h0, temperature=temperature, seed=seed, step_offset=step_offset,
-                  logits=logits, state=state, exec=exec, lse=lse, fixed_latent=fixed_latent)
+                  logits=logits, state=state, exec=exec, lse=lse, fixed_latent=fixed_latent,
+                  stress=stress, winners=winners)
     torch.cuda.synchronize()
     err = head.error()
     assert err == "WTS_OK", err
@@ -50,6 +51,8 @@ def run(head, t, *, base=None, x0=None, h0=None, temperature=0, seed=0, step_off
         res["state"] = o["state"].cpu().numpy()
     if lse:
         res["lse"] = o["lse"].cpu().numpy()
+    if winners:
+        res["winners"] = o["winners"].cpu().numpy().view(np.uint64)
     return res
 
 

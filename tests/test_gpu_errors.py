@@ -33,12 +33,13 @@ def _params(_abi, t, tokens, B, gamma, over):
     ("gamma above max_steps", {"gamma": 9}, 1),
     ("temperature 2", {"temperature": 2}, 1),
     ("negative step_offset", {"step_offset": -1}, 1),
-    ("unknown flag", {"flags": 2}, 1),
+    ("unknown flag", {"flags": 4}, 1),
     ("unknown exec", {"exec": 3}, 1),
     ("null tokens_out", {"tokens_out": None}, 1),
     ("null base", {"base": None}, 1),
     ("null x0", {"x0": None}, 1),
     ("odd base address", {"base": "odd"}, 1),
+    ("odd winners_out address", {"winners_out": "odd"}, 1),
 ])
 def test_walk_rejects_bad_arguments_and_leaves_outputs(case, kw, status):
     import torch
@@ -50,6 +51,8 @@ def test_walk_rejects_bad_arguments_and_leaves_outputs(case, kw, status):
     tokens = torch.full((4, 8), SENTINEL, dtype=torch.int32, device="cuda")
     if kw.get("base") == "odd":
         kw = {"base": t["base"].data_ptr() + 1}
+    if kw.get("winners_out") == "odd":
+        kw = {"winners_out": tokens.data_ptr() + 4}
     p = _params(_abi, t, tokens, B, gamma, kw)
     assert _abi.lib().wts_walk(h._h, ctypes.byref(p)) == status
     torch.cuda.synchronize()

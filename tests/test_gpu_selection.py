@@ -75,8 +75,8 @@ def _scenarios(tiles, G, shift):
     return out
 
 
-@pytest.fixture(scope="module")
-def crafted():
+def crafted_inputs():
+    """Inputs of the crafted scenarios (16 batch rows) and the hand winners."""
     d = datagen.make_inputs(V, 256, 16, GAMMA, seed=81)
     d["E"][:] = 0.0
     h, t = make_head(d)
@@ -102,6 +102,11 @@ def crafted():
         s_w[i] = -s_w[i]
     d["s_w"] = s_w
     return d, expected
+
+
+@pytest.fixture(scope="module")
+def crafted():
+    return crafted_inputs()
 
 
 def test_crafted_oracle_matches_hand_winners(crafted):
