@@ -64,8 +64,11 @@ def parse():
     ap.add_argument("--profile-walk", choices=sorted(PROFILE_WALKS),
                     help="run only the timed walks of one workload (for rocprofv3 runs)")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="with --profile: also run a plain 512 MiB device copy (known bytes) so a counter "
-                         "run can scale FETCH_SIZE / WRITE_SIZE")
+                    help="with --profile or --profile-walk: also run a plain 512 MiB device copy (known "
+                         "bytes) so a counter run can scale FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--kernel", default=HEADLINE_KERNEL,
+                    help="with --summarize-pmc / --summarize-counters: the kernel to summarize (another "
+                         "kernel than the headline's is printed, not written to the traffic file)")
     return ap.parse_args()
 
 
@@ -273,37 +276,39 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def summarize_pmc(fetch_csv, write_csv):
-    """Per-dispatch HBM bytes of the headline kernel from two counter runs, each
-    scaled by what the same counter reads for a plain copy of known size."""
+def summarize_pmc(fetch_csv, write_csv, kernel=HEADLINE_KERNEL):
+    """Per-dispatch HBM bytes of one kernel (the headline's by default) from two
+    counter runs, each scaled by what the same counter reads for a plain copy
+    of known size."""
     import csv
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        walk = [float(r["Counter_Value"]) for r in rows if HEADLINE_KERNEL in r["Kernel_Name"]]
+        walk = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
         calib_kib = max(copies)            # the 512 MiB copies are the largest copy dispatches
         factor = COPY_BYTES / (calib_kib * 1024.0)
         out[name] = {"walk_kib_per_dispatch": sum(walk) / len(walk), "dispatches": len(walk),
                      "copy_kib": calib_kib, "copy_bytes": COPY_BYTES, "scale": factor,
                      "walk_bytes_per_dispatch": sum(walk) / len(walk) * 1024.0 * factor}
-    res = {"kernel": HEADLINE_KERNEL, "workload": "markov-int8-v151936-r256-b1-g16-greedy",
-           "source_sha256": kernel_source_hash(), "counters": out,
+    res = {"kernel": kernel, "source_sha256": kernel_source_hash(), "counters": out,
            "traffic_bytes_per_launch": out["FETCH_SIZE"]["walk_bytes_per_dispatch"]
            + out["WRITE_SIZE"]["walk_bytes_per_dispatch"]}
-    with open(TRAFFIC_FILE, "w") as fh:
-        json.dump(res, fh, indent=1)
-    print(json.dumps(res))
+    if kernel == HEADLINE_KERNEL:
+        res["workload"] = "markov-int8-v151936-r256-b1-g16-greedy"
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
 
 
-def summarize_counters(path):
-    """Per-dispatch means of the counters of one --pmc pass over the headline kernel."""
+def summarize_counters(path, kernel=HEADLINE_KERNEL):
+    """Per-dispatch means of the counters of one --pmc pass over one kernel."""
     import csv
     vals = {}
     for r in csv.DictReader(open(path)):
-        if HEADLINE_KERNEL in r["Kernel_Name"]:
+        if kernel in r["Kernel_Name"]:
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    res = {"kernel": HEADLINE_KERNEL, "source_sha256": kernel_source_hash(),
+    res = {"kernel": kernel, "source_sha256": kernel_source_hash(),
            "dispatches": max((len(v) for v in vals.values()), default=0),
            "per_dispatch_mean": {k: sum(v) / len(v) for k, v in sorted(vals.items())}}
     print(json.dumps(res, indent=1))
@@ -377,10 +382,10 @@ def cpu_baseline(d, budget_s=12.0):
 def main():
     args = parse()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, kernel=args.kernel)
         return
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
+        summarize_counters(args.summarize_counters, kernel=args.kernel)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
@@ -393,6 +398,14 @@ def main():
 
     dev_name = torch.cuda.get_device_name(0)
     log("device", dev_name)
+    if args.copy_calib:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 536870912 bytes")
+        del src, dst
     if args.profile_walk:
         cfg, B_, g_, T_, ckw = PROFILE_WALKS[args.profile_walk]
         dp = datagen.config_inputs(cfg, B=B_, gamma=g_)
@@ -404,8 +417,10 @@ def main():
         hp.close()
         return
     import serial_draft_head_persistent_amd as wts
-    rf = wts.roofline(0)
-    log("measured denominators", rf)
+    rf = None
+    if not args.profile:
+        rf = wts.roofline(0)
+        log("measured denominators", rf)
     t_gen = time.perf_counter()
     d = datagen.config_inputs(1)
     t = dev_inputs(d)
@@ -415,14 +430,6 @@ def main():
     log("plan", plan)
 
     K, W = args.steps, args.warmup
-    if args.copy_calib:
-        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 536870912 bytes")
-        del src, dst
     ms_per_walk, us = timed_walks(head, t, K, W)
     log(f"resident walk: {ms_per_walk * 1e3:.2f} us (mean over {K}), median {np.median(us):.2f} us")
     if args.profile:
