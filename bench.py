@@ -164,6 +164,12 @@ def step_rooflines(plan, V, r, B, fit, rf):
     onchip_us = (w_reg / (operand_GBps * 1e9) + w_lds / (rf["lds_read_GBps"] * 1e9)) * 1e6
     floor_us = bound_us + rf["exchange_us"][0]
     useful_ops = 2.0 * 2 * V * r * B
+    # the same W share projected with v_dot4_i32_i8 instead: each instruction
+    # takes 4 W bytes per lane (256 B per wave) for one latent row, and hi and
+    # lo need one each; two waves per SIMD at the measured cycles per wave
+    # (the cross-lane sums of each row's partial products not counted)
+    dot4_instr_simd = tiles_simd * 16 * r / 256 * 2 * B
+    dot4_us = dot4_instr_simd * rf.get("dot4_2w_cycles", 0.0) / 2 / (rf["clock_MHz"] * 1e6) * 1e6
     return {
         "resident_step_roofline": {
             "bound": "mfma issue on the busiest SIMD, W operands on chip (measured MFMA rate)",
@@ -176,6 +182,11 @@ def step_rooflines(plan, V, r, B, fit, rf):
             "operand_rate_GBps": round(operand_GBps, 0), "lds_read_GBps": round(rf["lds_read_GBps"], 0),
             "achieved_GBps": round(w_bytes / (slope * 1e-6) / 1e9, 0),
             "bound_us": round(onchip_us, 3), "frac": round(onchip_us / slope, 4)},
+        "dot4_projection_bound": {
+            "bound": "the busiest SIMD's W share through v_dot4_i32_i8 (measured issue rate), a lower bound",
+            "dot4_per_simd_per_step": int(dot4_instr_simd),
+            "dot4_cycles_per_wave_2w": round(rf.get("dot4_2w_cycles", 0.0), 2),
+            "bound_us": round(dot4_us, 3), "vs_mfma_bound": round(dot4_us / bound_us, 2) if bound_us else None},
         "step_floor": {
             "bound": "resident-step bound + one selection round in isolation (both measured)",
             "exchange_round_us": round(rf["exchange_us"][0], 3), "floor_us": round(floor_us, 3),

@@ -58,6 +58,10 @@ typedef struct wts_roofline_result {
   double valu_indep_cycles;   /* the same over four independent chains           */
   double valu_indep_2w_cycles;/* the same per wave, two waves on each SIMD       */
   double valu_indep_4w_cycles;/* the same per wave, four waves on each SIMD      */
+  double dot4_2w_cycles;      /* shader cycles per v_dot4_i32_i8 (wave64) per
+                                 wave, four independent chains, two waves on
+                                 each SIMD (the int8 dot product a VALU
+                                 projection would use instead of the MFMA)      */
 } wts_roofline_result;
 
 wts_status wts_roofline(int32_t device, wts_roofline_result* out);

@@ -62,7 +62,7 @@ class RooflineResult(ctypes.Structure):
                 ("exchange_bad", ctypes.c_int64 * 6), ("hop_xcd_us", ctypes.c_double),
                 ("hop_device_us", ctypes.c_double), ("valu_dep_cycles", ctypes.c_double),
                 ("valu_indep_cycles", ctypes.c_double), ("valu_indep_2w_cycles", ctypes.c_double),
-                ("valu_indep_4w_cycles", ctypes.c_double)]
+                ("valu_indep_4w_cycles", ctypes.c_double), ("dot4_2w_cycles", ctypes.c_double)]
 
     def as_dict(self):
         out = {}

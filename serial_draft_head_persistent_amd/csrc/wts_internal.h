@@ -157,6 +157,6 @@ hipError_t launch_rf_exchange(int variant, int grid, int rounds, Ctrl* ctrl, uns
                               long long timeout, long long* clk, unsigned* wrong, hipStream_t s);
 hipError_t launch_rf_pingpong(int grid, int peer, int xcd, int rounds, unsigned long long* flag, long long timeout,
                               long long* clk, hipStream_t s);
-hipError_t launch_rf_valu(bool dep, int waves, int n, float* out, long long* clk, hipStream_t s);
+hipError_t launch_rf_valu(int mode, int waves, int n, float* out, long long* clk, hipStream_t s);
 
 }  // namespace wts

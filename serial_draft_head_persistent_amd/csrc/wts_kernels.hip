@@ -2324,31 +2324,41 @@ __global__ __launch_bounds__(64) void rf_pingpong_kernel(int peer, int xcd, int 
 // VALU issue: n dependent v_add_f32 per lane (one chain), or the same number
 // spread over four independent chains; s_memtime cycles per instruction, one
 // entry per wave (waves w and w + 4 of a workgroup share a SIMD).
-template <bool DEP>
+template <int MODE>
 __global__ __launch_bounds__(1024) void rf_valu_kernel(int n, float seed, float* out, long long* clk) {
+  // MODE 0: one dependent chain of v_add_f32; 1: four independent chains;
+  // 2: four independent chains of v_dot4_i32_i8 (the int8 dot product a
+  // VALU projection would use)
   float a0 = seed + threadIdx.x, a1 = a0 * 0.5f, a2 = a0 * 0.25f, a3 = a0 * 0.125f;
   const float d = seed * 1e-7f;
+  int i0 = (int)threadIdx.x, i1 = i0 ^ 5, i2 = i0 ^ 9, i3 = i0 ^ 17;
+  const int x = (int)(seed * 3.0f) | 0x01010101, y = x ^ 0x00FF00FF;
   const long long t0 = (long long)__builtin_amdgcn_s_memtime();
   for (int i = 0; i < n; i += 16) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (DEP) {
+      if (MODE == 0) {
         a0 = a0 + d;
         a0 = a0 + d;
         a0 = a0 + d;
         a0 = a0 + d;
-      } else {
+      } else if (MODE == 1) {
         a0 = a0 + d;
         a1 = a1 + d;
         a2 = a2 + d;
         a3 = a3 + d;
+      } else {
+        i0 = __builtin_amdgcn_sdot4(x, y, i0, false);
+        i1 = __builtin_amdgcn_sdot4(x, y, i1, false);
+        i2 = __builtin_amdgcn_sdot4(x, y, i2, false);
+        i3 = __builtin_amdgcn_sdot4(x, y, i3, false);
       }
-      asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+      asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(i0), "+v"(i1), "+v"(i2), "+v"(i3));
     }
   }
   const long long t1 = (long long)__builtin_amdgcn_s_memtime();
   if ((threadIdx.x & 63) == 0) clk[threadIdx.x >> 6] = t1 - t0;
-  out[threadIdx.x] = a0 + a1 + a2 + a3;
+  out[threadIdx.x] = a0 + a1 + a2 + a3 + (float)(i0 ^ i1 ^ i2 ^ i3);
 }
 
 hipError_t launch_rf_lds(int grid, int rounds, unsigned* out, hipStream_t s) {
@@ -2381,9 +2391,10 @@ hipError_t launch_rf_pingpong(int grid, int peer, int xcd, int rounds, unsigned 
   rf_pingpong_kernel<<<grid, 64, 0, s>>>(peer, xcd, rounds, flag, timeout, clk);
   return hipGetLastError();
 }
-hipError_t launch_rf_valu(bool dep, int waves, int n, float* out, long long* clk, hipStream_t s) {
-  if (dep) rf_valu_kernel<true><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
-  else rf_valu_kernel<false><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
+hipError_t launch_rf_valu(int mode, int waves, int n, float* out, long long* clk, hipStream_t s) {
+  if (mode == 0) rf_valu_kernel<0><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
+  else if (mode == 1) rf_valu_kernel<1><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
+  else rf_valu_kernel<2><<<1, 64 * waves, 0, s>>>(n, 1.5f, out, clk);
   return hipGetLastError();
 }
 

@@ -181,15 +181,16 @@ extern "C" wts_status wts_roofline(int32_t device, wts_roofline_result* out) {
     if (st == WTS_OK) st = hop(other, 0, &out->hop_device_us);
     if (st != WTS_OK) return st;
   }
-  // VALU issue: one wave, then eight and sixteen waves (two and four per SIMD) of one workgroup
+  // VALU issue: one wave, then eight and sixteen waves (two and four per SIMD)
+  // of one workgroup; then v_dot4_i32_i8 at two waves per SIMD
   {
     const int n = 1 << 20;
     float* fo = bufs.get<float>(1024 * sizeof(float));
     if (!fo) return WTS_ERR_NO_MEMORY;
-    auto run = [&](bool dep, int waves, double* res) -> wts_status {
+    auto run = [&](int mode, int waves, double* res) -> wts_status {
       std::vector<long long> hc(waves);
-      if (launch_rf_valu(dep, waves, n, fo, clk, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-          launch_rf_valu(dep, waves, n, fo, clk, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+      if (launch_rf_valu(mode, waves, n, fo, clk, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+          launch_rf_valu(mode, waves, n, fo, clk, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
           hipMemcpy(hc.data(), clk, waves * sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
         return WTS_ERR_DEVICE;
       double m = 0.0;
@@ -197,10 +198,11 @@ extern "C" wts_status wts_roofline(int32_t device, wts_roofline_result* out) {
       *res = m / n;
       return WTS_OK;
     };
-    wts_status st = run(true, 1, &out->valu_dep_cycles);
-    if (st == WTS_OK) st = run(false, 1, &out->valu_indep_cycles);
-    if (st == WTS_OK) st = run(false, 8, &out->valu_indep_2w_cycles);
-    if (st == WTS_OK) st = run(false, 16, &out->valu_indep_4w_cycles);
+    wts_status st = run(0, 1, &out->valu_dep_cycles);
+    if (st == WTS_OK) st = run(1, 1, &out->valu_indep_cycles);
+    if (st == WTS_OK) st = run(1, 8, &out->valu_indep_2w_cycles);
+    if (st == WTS_OK) st = run(1, 16, &out->valu_indep_4w_cycles);
+    if (st == WTS_OK) st = run(2, 8, &out->dot4_2w_cycles);
     if (st != WTS_OK) return st;
   }
   return hipDeviceSynchronize() == hipSuccess ? WTS_OK : WTS_ERR_DEVICE;

@@ -27,3 +27,4 @@ def test_roofline_measurements():
         assert r["exchange_us"][0] > r["hop_xcd_us"] + 0.5 * r["hop_device_us"]
     # a wave issues at most one VALU instruction per cycle
     assert r["valu_dep_cycles"] >= 1 and r["valu_indep_cycles"] >= 1 and r["valu_indep_4w_cycles"] >= 1
+    assert r["dot4_2w_cycles"] >= 1
