@@ -170,8 +170,12 @@ typedef struct wts_plan {
  * rows (V / grid; the local selection key holds a 16-bit row). */
 wts_status wts_create(const wts_create_params* p, wts_ctx** out);
 
-/* Enqueue one walk on p->stream (asynchronous; inputs must stay alive and
- * unmodified until the stream reaches the walk's end).  Writes tokens_out
+/* Enqueue one walk on p->stream: gamma serial draft steps of the head
+ * (Fig. 2), each a projection of the latent against W, the epilogue of
+ * Fig. 7, a selection across all workgroups (Fig. 8) and the state advance,
+ * with the shard of W kept on chip for the whole walk (Fig. 1; or streamed,
+ * Fig. 4/11, per exec).  Asynchronous; inputs must stay alive and
+ * unmodified until the stream reaches the walk's end.  Writes tokens_out
  * [b][t] = token chosen at step t, and optionally logits_out and state_out.
  * The walk keeps no host-side state between calls (the control block's
  * parity advances on the device), so a walk captured in a HIP graph may be
@@ -202,15 +206,17 @@ wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p);
 #define WTS_NOALLOC_LSE_BYTES (1 << 20)
 wts_status wts_walk_noalloc(wts_ctx* ctx, const wts_walk_params* p);
 
-/* Synchronizes the device, then frees everything the context owns.
- * NULL is ignored. */
+/* Synchronizes the device, then frees everything the context owns (the
+ * repacked W that each walk loads on chip, Fig. 1, the quantised embedding
+ * rows and the control block of the selection, Fig. 8).  NULL is ignored. */
 void wts_destroy(wts_ctx* ctx);
 
 /* Synchronizes the device and returns the error latched by walks since the
  * last clear (WTS_OK if none).  clear != 0 resets the latch. */
 wts_status wts_get_error(wts_ctx* ctx, int clear);
 
-/* Residency a walk of B batch rows under `exec` and `temperature` uses, when
+/* Residency (registers, LDS, streamed; Fig. 12 placement, Fig. 10 and 14
+ * partial residency) a walk of B batch rows under `exec` and `temperature` uses, when
  * it asks for no lse_out (B selects the batch bucket 1, 2, 4, 8 or 16; larger
  * buckets keep fewer tiles in registers; T=1 Markov walks keep the next step's
  * noise in LDS, which can leave room for fewer LDS tiles).  A Markov walk
