@@ -118,6 +118,7 @@ struct WalkArgs {
   unsigned seed_hi;
   int step;                // step-wise launches: the step this launch runs
   const uint16_t* base;
+  unsigned base_bytes;     // 2 B gamma V: the base logits' bytes (below 2^32)
   const int* x0;
   const float* h0;
   int* tokens;

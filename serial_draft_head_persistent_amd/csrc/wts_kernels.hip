@@ -355,6 +355,12 @@ constexpr int kOffRecRows = 12288;                 // recurrent, one batch row: 
 constexpr int kRecRowBytes = kR * 4;
 
 
+// Raw buffer resource over [p, p + bytes): loads at byte offsets >= bytes
+// return 0.  Word 3 as for untyped loads on gfx9 (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ v4i mma(const v4i& a, const v4i& b, const v4i& c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
@@ -648,23 +654,33 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
 // Base logits of one result entry set (bf16 bits), zero where unused.  The
 // row index is made opaque so that the per-lane addresses are recomputed at
 // every step instead of being kept in registers for the whole walk.
+//
+// Buffer loads: element (b, t, v) sits at byte 2 ((b gamma + t) V + v) of
+// the base logits, and the batch row of entry e of M block m is the lane's
+// first row lb = bent(0, 0) plus m RPS / LPB + e, so one offset per call
+// and one add per entry address every entry.  Every lane loads, so the loads
+// are straight-line code and nothing waits for them before their use; a
+// buffer load past the end (a batch row >= B) returns 0, and the epilogue
+// drops the pairs that do not exist (`ok` false, or a row >= B).
 template <int WT, int BB>
 __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                           int v, bool ok, uint32_t (&bv)[Geo<WT, BB>::NE]) {
   using Gm = Geo<WT, BB>;
-  asm volatile("" : "+v"(v));
+  (void)ok;
+  int lb = ro.bent(0, 0);
+  asm volatile("" : "+v"(v), "+v"(lb));
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.base, a.base_bytes);
+  const uint32_t plane = (uint32_t)a.gamma * (uint32_t)a.V;  // elements per batch row
+  const uint32_t off = 2u * ((uint32_t)lb * plane + (uint32_t)t * (uint32_t)a.V + (uint32_t)v);
 #pragma unroll
   for (int e = 0; e < Gm::NE; ++e) {
-    const int b = ro.bent(m, e);
-    if (b >= BB) {  // compile-time: entry unused by this batch bucket
+    const int u = m * Gm::RPS / Gm::LPB + e;  // batch row bent(m, e) - lb, known at compile time
+    if (u >= BB) {  // no lane's entry e is a row of this batch bucket
       bv[e] = 0u;
       continue;
     }
-    // Every lane loads (element 0 where the pair does not exist; the epilogue
-    // drops such pairs), so the loads are straight-line code and nothing
-    // waits for them before their use.
-    const bool use = ok && b < a.B;
-    bv[e] = a.base[use ? ((size_t)b * a.gamma + t) * a.V + v : 0];
+    // unconditional: a lane whose row is >= B reads past the buffer, i.e. 0
+    bv[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 2u * (uint32_t)u * plane, 0, 0);
   }
 }
 
@@ -701,7 +717,10 @@ __device__ __forceinline__ void fetch_tile(const WalkArgs& a, const Roles<WT, BB
   }
   const int v = tile * kTileRows + ro.n;
   const bool ok = ro.cslot == 0 && v < a.V;
-  d.sw = WT == 0 ? a.sw[ok ? v : 0] : 0.0f;  // every lane loads (see load_base)
+  // every lane loads (see load_base); rows past the padded scales read 0
+  d.sw = WT == 0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  buf_rsrc(a.sw, (uint32_t)a.tiles * kTileRows * 4u), 4u * (uint32_t)v, 0, 0))
+                 : 0.0f;
 #pragma unroll
   for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, v, ok, d.bv[m]);
 }
@@ -1419,7 +1438,9 @@ __device__ __forceinline__ BaseTouch touch_base(const WalkArgs& a, int t, int ro
       if (q < a.B * nl) {
         const int b = q / nl, l = q % nl;
         const int v = l + 1 == nl ? r1 - 1 : row0 + 64 * l;
-        r.v[k] = a.base[((size_t)b * a.gamma + t) * a.V + v];
+        r.v[k] = __builtin_amdgcn_raw_buffer_load_b16(
+            buf_rsrc(a.base, a.base_bytes), 2u * (((uint32_t)b * (uint32_t)a.gamma + (uint32_t)t) * (uint32_t)a.V + (uint32_t)v),
+            0, 0);
       }
     }
   }
@@ -1505,7 +1526,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
 
   // Base logits of the register-resident groups and the first non-register
   // tile are loaded one step ahead, so their memory latency overlaps the
-  // previous step's exchange (step 0's: the shard load).
+  // previous step's exchange.
   uint32_t bnx[Gm::NG][Gm::NM][Gm::NE];
   // FULL: LDS tiles in slot groups like the register tiles, base logits loaded ahead
   constexpr int NLG = FULL ? (kFullLdsMax + Gm::S - 1) / Gm::S : 1;
@@ -1528,7 +1549,6 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
         for (int m = 0; m < Gm::NM; ++m) load_base<WT, BB>(a, ro, t, m, lv(gl), lok(gl), bnl[gl][m]);
     }
   };
-  fetch_base(0);
 
   for (int i = 0; i < nlds; ++i) {
     const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * (nreg + i)) * Gm::CH * 64 + ro.lane;
@@ -1582,6 +1602,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   __syncthreads();
   if (e0_touch == 0x9E3779B1u) *(lds + kOffFlag + 4) = 1;  // keeps the touch; the byte is never read
   if (*sflag) return;
+  fetch_base(0);
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
   if (HEAD == kHeadMarkov && CAND && fixed) {
     // the probe's latent, staged once where later steps read staged rows

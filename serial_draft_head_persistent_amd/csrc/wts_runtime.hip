@@ -381,6 +381,8 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
       ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3) || ((uintptr_t)p->winners_out & 7))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
+  // the kernels address the base logits with 32-bit byte offsets
+  if (2ull * (unsigned long long)p->B * p->gamma * ctx->V > 0xFFFFFFFFull) return WTS_ERR_UNSUPPORTED;
   // the forced delays and the winner record belong to the persistent kernel's exchange
   if (p->exec == WTS_EXEC_STEPWISE && ((p->flags & WTS_WALK_STRESS) || p->winners_out)) return WTS_ERR_UNSUPPORTED;
   {
@@ -421,6 +423,7 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   a.seed_lo = (unsigned)(p->seed & 0xFFFFFFFFull);
   a.seed_hi = (unsigned)(p->seed >> 32);
   a.base = p->base;
+  a.base_bytes = (unsigned)(2ull * p->B * p->gamma * ctx->V);
   a.x0 = p->x0;
   a.h0 = p->h0;
   a.tokens = p->tokens_out;
