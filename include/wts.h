@@ -182,9 +182,7 @@ wts_status wts_create(const wts_create_params* p, wts_ctx** out);
  * replayed; the captured pointers' contents may change between replays.
  * WTS_ERR_UNSUPPORTED (before any launch) if the LDS a T=1 Markov walk needs
  * for one step of Gumbel noise (4 bytes per batch row and vocabulary row of a
- * workgroup) does not fit beside the kernel's other LDS data, or if the base
- * logits span 2^32 bytes or more (2 B gamma V; the kernels address them with
- * 32-bit offsets). */
+ * workgroup) does not fit beside the kernel's other LDS data. */
 wts_status wts_walk(wts_ctx* ctx, const wts_walk_params* p);
 
 /* For callers that cannot allocate device memory (code under HIP graph

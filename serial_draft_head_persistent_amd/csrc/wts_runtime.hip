@@ -239,6 +239,11 @@ const char* wts_status_string(wts_status s) {
   return "unknown status";
 }
 
+// The kernels address the base logits (2 B gamma V bytes) with 32-bit byte
+// offsets; the limits on V (18-bit token field of the selection key), B and
+// gamma keep them far below 2^32.
+static_assert(2ull * kMaxB * kMaxSteps * 262143ull < (1ull << 32), "base logits within 32-bit offsets");
+
 wts_status wts_create(const wts_create_params* p, wts_ctx** out) {
   if (!p || !out) return WTS_ERR_INVALID_ARG;
   *out = nullptr;
@@ -381,8 +386,6 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
       ((uintptr_t)p->trace_out & 7) || ((uintptr_t)p->lse_out & 3) || ((uintptr_t)p->winners_out & 7))
     return WTS_ERR_INVALID_ARG;
   if (p->exec == WTS_EXEC_STEPWISE && ctx->head != WTS_HEAD_MARKOV) return WTS_ERR_UNSUPPORTED;
-  // the kernels address the base logits with 32-bit byte offsets
-  if (2ull * (unsigned long long)p->B * p->gamma * ctx->V > 0xFFFFFFFFull) return WTS_ERR_UNSUPPORTED;
   // the forced delays and the winner record belong to the persistent kernel's exchange
   if (p->exec == WTS_EXEC_STEPWISE && ((p->flags & WTS_WALK_STRESS) || p->winners_out)) return WTS_ERR_UNSUPPORTED;
   {

@@ -76,31 +76,3 @@ def test_plan_rejects_bad_arguments():
     assert plan.grid >= 1 and plan.tiles * 16 >= d["W"].shape[0]
     h.close()
 
-
-def test_base_logits_beyond_32_bit_offsets_rejected():
-    # The kernels address the base logits with 32-bit byte offsets: a walk whose
-    # base logits span 2^32 bytes or more (2 B gamma V) is refused before any
-    # launch.  V = 2,100,000 rows at 16 rows and 64 steps is 4.3e9 bytes (63
-    # steps would fit).  W and E are zeros: no walk runs on them.
-    import torch
-    from serial_draft_head_persistent_amd import Head, _abi
-    V = 2_100_000
-    print("CASE base_bytes_limit V", V, flush=True)
-    W = torch.zeros((V, 256), dtype=torch.int8, device="cuda")
-    ws = torch.ones(V, dtype=torch.float32, device="cuda")
-    E = torch.zeros((V, 256), dtype=torch.float32, device="cuda")
-    h = Head(W, E, w_scale=ws, head="markov", max_batch=16, max_steps=64)
-    base = torch.zeros(64, dtype=torch.int16, device="cuda")
-    x0 = torch.zeros(16, dtype=torch.int32, device="cuda")
-    tokens = torch.full((16, 64), SENTINEL, dtype=torch.int32, device="cuda")
-    p = _abi.WalkParams(B=16, gamma=64, step_offset=0, temperature=0, seed=0,
-                        base=base.data_ptr(), x0=x0.data_ptr(), h0=None,
-                        tokens_out=tokens.data_ptr(), logits_out=None, state_out=None, exec=0, flags=0,
-                        stream=ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
-                        trace_out=None, lse_out=None)
-    assert 2 * 16 * 64 * V >= 1 << 32 > 2 * 16 * 63 * V
-    assert _abi.lib().wts_walk(h._h, ctypes.byref(p)) == 2      # WTS_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
-    assert h.error() == "WTS_OK"
-    assert (tokens.cpu().numpy() == SENTINEL).all()
-    h.close()
