@@ -21,18 +21,19 @@
 //    accumulators, and the lanes of result slot s take tile s, so all 64 lanes
 //    of the result carry useful logits;
 //  * W tiles live in registers, then LDS, and the remainder streams from HBM
-//    each step with one tile of prefetch; a whole-shard variant (bf16, one
-//    batch row) drops the streaming buffers to hold more tiles in registers;
+//    each step with one or two tiles of prefetch; a whole-shard variant (bf16,
+//    up to four batch rows) drops the streaming buffers to hold more tiles in
+//    registers;
 //  * the cross-workgroup selection is a two-level all-gather of step-tagged
 //    64-bit keys (one line per workgroup, a group leader per 16 workgroups,
 //    one line per group and XCD), polled by one wave per workgroup with a
 //    wall-clock watchdog.  The first level stays inside one XCD's L2.  Fig. 8
 //    has each worker atomically update one maximum and an arrival count; on
 //    MI355X that serialises 2 x 256 device-scope atomics per step (measured
-//    ~11 us per step), and the all-gather needs none.
+//    about 10 us per round), and the all-gather needs none.
 //
-// Bit-exactness with the host reference needs: no contraction of a*b+c
-// (built with -ffp-contract=off), IEEE division (default), rintf half-even.
+// Bit-exactness with the oracle needs: no contraction of a*b+c (built with
+// -ffp-contract=off), IEEE division (default), rintf half-even.
 
 #include "wts_internal.h"
 
