@@ -602,7 +602,7 @@ struct LseAcc<NM, NE, false> {
 template <int WT, int BB, int TEMP, bool NZ, bool LS, bool GP = false>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                          const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
-                                         float sw, const uint32_t (&bv)[Geo<WT, BB>::NE],
+                                         float sw, const uint16_t (&bv)[Geo<WT, BB>::NE],
                                          const float (&shi)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                          typename LKey<TEMP>::T (&best)[Geo<WT, BB>::NM][Geo<WT, BB>::NE],
                                          LseAcc<Geo<WT, BB>::NM, Geo<WT, BB>::NE, LS>& ls,
@@ -622,7 +622,7 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
     } else {
       z = acc[e];
     }
-    z = z + bf16_f32(bv[e]);
+    z = z + bf16_f32((uint32_t)bv[e]);
     // bf16 rounding to nearest even: the upper half of r is the logit
     const uint32_t zb = __float_as_uint(z);
     const uint32_t r = zb + 0x7FFFu + ((zb >> 16) & 1u);
@@ -665,7 +665,7 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
 // drops the pairs that do not exist (`ok` false, or a row >= B).
 template <int WT, int BB>
 __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
-                                          int v, bool ok, uint32_t (&bv)[Geo<WT, BB>::NE]) {
+                                          int v, bool ok, uint16_t (&bv)[Geo<WT, BB>::NE]) {
   using Gm = Geo<WT, BB>;
   (void)ok;
   int lb = ro.bent(0, 0);
@@ -677,7 +677,7 @@ __device__ __forceinline__ void load_base(const WalkArgs& a, const Roles<WT, BB>
   for (int e = 0; e < Gm::NE; ++e) {
     const int u = m * Gm::RPS / Gm::LPB + e;  // batch row bent(m, e) - lb, known at compile time
     if (u >= BB) {  // no lane's entry e is a row of this batch bucket
-      bv[e] = 0u;
+      bv[e] = 0;
       continue;
     }
     // unconditional: a lane whose row is >= B reads past the buffer, i.e. 0
@@ -691,7 +691,7 @@ template <int WT, int BB>
 struct TileBuf {
   v4i w[Geo<WT, BB>::CH];
   float sw;
-  uint32_t bv[Geo<WT, BB>::NM][Geo<WT, BB>::NE];
+  uint16_t bv[Geo<WT, BB>::NM][Geo<WT, BB>::NE];  // bf16 bits, widened where used
 };
 
 // Load wave-local tile i (from LDS for i < i0 + nlds, else from memory) for
@@ -1480,8 +1480,10 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   Ctrl* ctrl = a.ctrl;
   // The walk's epoch and the first state are requested before the shard, so
   // that their latency overlaps the shard load instead of preceding it.
-  const unsigned epoch_v = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int x0_v = tid < a.B ? a.x0[tid] : 0;
+  unsigned epoch_v = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // (straight-line loads throughout the prologue: a load under a branch makes
+  // the compiler wait for every load before it at the first use of any)
+  int x0_v = a.x0[tid < a.B ? tid : 0];
   constexpr bool CAND = stage_candidates(HEAD, WT, BB);
   constexpr bool NOISE = TEMP && HEAD == kHeadMarkov;  // noise one step ahead in LDS
   // fixed-latent probe (Fig. 13b): the state is never advanced after step 0
@@ -1502,12 +1504,16 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   char* ldsw = lds + scratch + (size_t)lds_before * TB;
 
   // One-time shard load (Fig. 4 entry cost): register tiles, then LDS tiles.
+  // Every register tile is loaded; one that this wave does not own reads the
+  // last tile of W instead (its results are dropped: no row of a slot beyond
+  // nreg is ever selected or written).
   v4i wr[Gm::RT][Gm::CH];
 #pragma unroll
   for (int i = 0; i < Gm::RT; ++i) {
-    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * i) * Gm::CH * 64 + ro.lane;
+    const int tile = i < nreg ? tb + w + NW * i : a.tiles - 1;
+    const v4i* p = (const v4i*)a.Wp + (size_t)tile * Gm::CH * 64 + ro.lane;
 #pragma unroll
-    for (int c = 0; c < Gm::CH; ++c) wr[i][c] = (i < nreg) ? p[c * 64] : v4i{0, 0, 0, 0};
+    for (int c = 0; c < Gm::CH; ++c) wr[i][c] = p[c * 64];
   }
   // vocabulary row of this lane's result in register group gi, and whether it exists
   // (opaque to the compiler, so that values derived from it are recomputed at
@@ -1520,7 +1526,14 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   auto gok = [&](int gi) { return gi * Gm::S + ro.cslot < nreg && gv(gi) < a.V; };
   float gsw[WT == 0 ? Gm::NG : 1];  // row scales of the register groups (int8)
 #pragma unroll
-  for (int gi = 0; gi < (WT == 0 ? Gm::NG : 1); ++gi) gsw[gi] = (WT == 0 && gok(gi)) ? a.sw[gv(gi)] : 0.0f;
+  for (int gi = 0; gi < (WT == 0 ? Gm::NG : 1); ++gi)  // rows past the padded scales read 0
+    gsw[gi] = WT == 0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       buf_rsrc(a.sw, (uint32_t)a.tiles * kTileRows * 4u),
+                                                       4u * (uint32_t)gv(gi), 0, 0))
+                      : 0.0f;
+  // (the empty asm keeps the uses of the epoch and of the first state, and
+  // the waits for them, behind the shard's loads in program order)
+  asm volatile("" : "+v"(epoch_v), "+v"(x0_v)::"memory");
   const int row0 = tb * kTileRows;  // first vocabulary row of this workgroup
   float* noise_lds = NOISE ? (float*)(lds + a.noise_off) : nullptr;
   const float* noise = noise_lds;
@@ -1528,7 +1541,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   // Base logits of the register-resident groups and the first non-register
   // tile are loaded one step ahead, so their memory latency overlaps the
   // previous step's exchange.
-  uint32_t bnx[Gm::NG][Gm::NM][Gm::NE];
+  uint16_t bnx[Gm::NG][Gm::NM][Gm::NE];
   // FULL: LDS tiles in slot groups like the register tiles, base logits loaded ahead
   constexpr int NLG = FULL ? (kFullLdsMax + Gm::S - 1) / Gm::S : 1;
   auto lv = [&](int gl) {
@@ -1537,7 +1550,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     return v;
   };
   auto lok = [&](int gl) { return gl * Gm::S + ro.cslot < nlds && lv(gl) < a.V; };
-  uint32_t bnl[NLG][Gm::NM][Gm::NE];
+  uint16_t bnl[NLG][Gm::NM][Gm::NE];
   auto fetch_base = [&](int t) {
 #pragma unroll
     for (int gi = 0; gi < Gm::NG; ++gi)
@@ -1551,19 +1564,15 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     }
   };
 
-  for (int i = 0; i < nlds; ++i) {
-    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * (nreg + i)) * Gm::CH * 64 + ro.lane;
-#pragma unroll
-    for (int c = 0; c < Gm::CH; ++c) *(v4i*)(ldsw + (size_t)i * TB + c * 1024 + ro.lane * 16) = p[c * 64];
-  }
-
+  // While the shard is in flight (only the epoch and the first state, loaded
+  // before it, are waited for here): the flags, the first state with its
+  // check (rows tid < B, all in wave 0, after the flag's reset in program
+  // order) and the candidate slots.
+  const int par = __builtin_amdgcn_readfirstlane((int)(epoch_v & 1u));
   if (tid == 0) {
     *sflag = 0;
     *lcnt = 0;
   }
-  // the first state (rows tid < B, all in wave 0, after the flag's reset in
-  // program order); its embedding row is pulled into the L2 for step 0
-  uint32_t e0_touch = 0;
   if (tid < a.B) {
     int x = x0_v;
     if (x < 0 || x >= a.V) {
@@ -1572,15 +1581,17 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
       x = 0;
     }
     sx[tid] = x;
-    if (HEAD == kHeadMarkov) {
-      const uint32_t* er = WT == 0 ? (const uint32_t*)(a.Eq + (size_t)x * 512) : (const uint32_t*)(a.Eb + (size_t)x * kR);
-      e0_touch = er[0] ^ er[32] ^ er[64] ^ er[96];
-    }
   }
   if (CAND) {
     for (int i = tid; i < 64; i += NT) ((int*)(lds + kOffZero))[i] = 0;
     for (int i = tid; i < kGroups * 2; i += NT) ((unsigned long long*)(lds + kOffCand))[i] = 0ull;
     if (tid == 0) *(int*)(lds + kOffDone) = 0;
+  }
+
+  for (int i = 0; i < nlds; ++i) {
+    const v4i* p = (const v4i*)a.Wp + (size_t)(tb + w + NW * (nreg + i)) * Gm::CH * 64 + ro.lane;
+#pragma unroll
+    for (int c = 0; c < Gm::CH; ++c) *(v4i*)(ldsw + (size_t)i * TB + c * 1024 + ro.lane * 16) = p[c * 64];
   }
   float racc[BB];
   float cj = 0.0f;
@@ -1597,11 +1608,11 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     if (tid >= kThreads - kR) cj = a.c[tid - (kThreads - kR)];
   }
   if (NOISE) make_noise(a, noise_lds, 0, row0, cnt * kTileRows, tid, NT);
-  // the other parity's lines, for the next walk (nothing reads them in this one)
-  const int par = __builtin_amdgcn_readfirstlane((int)(epoch_v & 1u));
+  // the other parity's lines, for the next walk (nothing reads them in this
+  // one); after the LDS tiles, whose loads would otherwise wait for these
+  // stores as well
   clear_next_walk<true, NT>(ctrl, par);
   __syncthreads();
-  if (e0_touch == 0x9E3779B1u) *(lds + kOffFlag + 4) = 1;  // keeps the touch; the byte is never read
   if (*sflag) return;
   fetch_base(0);
   if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
