@@ -535,7 +535,8 @@ def main():
                 m, u = timed_walks(head, tb, 50, 5, temperature=T, seed=0)
                 sweep.append({"B": B_, "gamma": 16, "T": T, "median_us": round(float(np.median(u)), 2),
                               "plan_reg_lds_stream": [head.plan(B_, temperature=T)[k]
-                                                     for k in ("reg_tiles", "lds_tiles", "stream_tiles")]})
+                                                     for k in ("reg_tiles", "lds_tiles", "stream_tiles")],
+                              "phases": breakdown(head, tb, reps=10, temperature=T, seed=0)})
             log("sweep B", B_, sweep[-2:])
         extras["sweep_markov_int8_v151936"] = sweep
         # T=1 Gumbel noise against its VALU bound: B x V values per step, each
@@ -579,7 +580,8 @@ def main():
             p3 = h3.plan(B_)
             r3.append({"B": B_, "median_us": round(float(np.median(u)), 2),
                        "resident_MB": round(p3["resident_bytes"] / 1e6, 1),
-                       "streamed_MB_per_step": round(p3["streamed_bytes"] / 1e6, 1)})
+                       "streamed_MB_per_step": round(p3["streamed_bytes"] / 1e6, 1),
+                       "phases": breakdown(h3, tb, reps=10)})
         extras["markov_bf16_v248320"] = r3
         log("bf16 248k", r3)
         # the partially resident sixteen-row walk against the stream rates
