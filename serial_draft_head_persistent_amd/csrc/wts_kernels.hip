@@ -356,6 +356,10 @@ constexpr int kOffRecRows = 12288;                 // recurrent, one batch row: 
 constexpr int kRecRowBytes = kR * 4;
 
 
+#ifndef WTS_PIN_FULL
+#define WTS_PIN_FULL 7
+#endif
+
 // Raw buffer resource over [p, p + bytes): loads at byte offsets >= bytes
 // return 0.  Word 3 as for untyped loads on gfx9 (32-bit data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
@@ -1626,6 +1630,18 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     }
   }
 
+  // One wave per SIMD: the register tiles live in the AGPRs, from which the
+  // MFMAs read their B operands directly (without this the compiler keeps
+  // them as VGPR values parked in AGPRs and copies each 16-byte chunk back to
+  // VGPRs before every use: 4 VALU instructions per MFMA).
+  if constexpr (NW == 4) {
+    // (the whole-shard variant holds more tiles than the AGPRs: those that fit)
+    constexpr int PIN = FULL ? WTS_PIN_FULL : Gm::RT;
+#pragma unroll
+    for (int i = 0; i < PIN; ++i)
+#pragma unroll
+      for (int c = 0; c < Gm::CH; ++c) asm volatile("" : "+a"(wr[i][c]));
+  }
   // per-step phase stamps (workgroup view of wave 0)
   auto stamp = [&](int t, int k) {
     if (a.trace && tid == 0) a.trace[((size_t)t * G + g) * 4 + k] = wall_clock64();
