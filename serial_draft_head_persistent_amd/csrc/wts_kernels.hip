@@ -1716,30 +1716,20 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
           constexpr bool SPLIT = WT == 0 && Gm::S == 1;
 #pragma unroll
           for (int s = 0; s < Gm::S; ++s) accs[s] = AT{0, 0, 0, 0};
-          if ((gi + 1) * Gm::S <= nreg && (gi + 1) * Gm::S <= Gm::RT) {
-            // a full group: chunk-major over its S tiles
+          // chunk-major over the group's register tiles (independent MFMA
+          // chains); a slot past this wave's tiles holds a copy of the last
+          // tile of W, whose results are never selected (gok), so the group's
+          // tiles are computed without a run-time test
 #pragma unroll
-            for (int c = 0; c < Gm::CH; ++c)
-#pragma unroll
-              for (int s = 0; s < Gm::S; ++s) {
-                const int i = gi * Gm::S + s < Gm::RT ? gi * Gm::S + s : 0;
-                if (SPLIT && (c & 1)) acc2 = mma(lat[m][c], wr[i][c], acc2);
-                else accs[s] = mma(lat[m][c], wr[i][c], accs[s]);
-              }
-          } else {
-            // the last, partial group: its first tiles, one after another
+          for (int c = 0; c < Gm::CH; ++c)
 #pragma unroll
             for (int s = 0; s < Gm::S; ++s) {
               const int i = gi * Gm::S + s;
-              if (i < Gm::RT && i < nreg) {
-#pragma unroll
-                for (int c = 0; c < Gm::CH; ++c) {
-                  if (SPLIT && (c & 1)) acc2 = mma(lat[m][c], wr[i < Gm::RT ? i : 0][c], acc2);
-                  else accs[s] = mma(lat[m][c], wr[i < Gm::RT ? i : 0][c], accs[s]);
-                }
+              if (i < Gm::RT) {  // compile-time: the slots that exist in registers
+                if (SPLIT && (c & 1)) acc2 = mma(lat[m][c], wr[i][c], acc2);
+                else accs[s] = mma(lat[m][c], wr[i][c], accs[s]);
               }
             }
-          }
           AT acc = pick_slot<Gm::S>(accs, ro.cslot);
           if (SPLIT) acc = acc + acc2;
           epilogue<WT, BB, TEMP, NOISE, LS, GP>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
