@@ -40,6 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
 # T, create kwargs)), for rocprofv3 kernel traces and counter passes.
 PROFILE_WALKS = {
     "markov-int8-v151936-b1-g16": (1, 1, 16, 0, {}),
+    "markov-bf16-v248320-b1-g16": (3, 1, 16, 0, {}),
     "markov-bf16-v248320-b16-g16": (3, 16, 16, 0, {}),
     "markov-int8-v151936-b16-g16-partial": (2, 16, 16, 0, {"resident_tiles": 2, "lds_tiles": 0}),
     "markov-int8-v151936-b16-g16-t1": (2, 16, 16, 1, {}),
