@@ -1750,13 +1750,24 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
             AT accs[Gm::S];
 #pragma unroll
             for (int s = 0; s < Gm::S; ++s) accs[s] = AT{0, 0, 0, 0};
+            auto lds_chunk = [&](int s, int c) {
+              return *(const v4i*)(ldsw + (size_t)(gl * Gm::S + s) * TB + c * 1024 + ro.lane * 16);
+            };
+            if ((gl + 1) * Gm::S <= nlds) {
+              // a full group: chunk-major, no per-MFMA test
 #pragma unroll
-            for (int c = 0; c < Gm::CH; ++c)
+              for (int c = 0; c < Gm::CH; ++c)
+#pragma unroll
+                for (int s = 0; s < Gm::S; ++s) accs[s] = mma(lat[m][c], lds_chunk(s, c), accs[s]);
+            } else {
+              // the last, partial group: one test per tile
 #pragma unroll
               for (int s = 0; s < Gm::S; ++s)
-                if (gl * Gm::S + s < nlds)
-                  accs[s] = mma(lat[m][c], *(const v4i*)(ldsw + (size_t)(gl * Gm::S + s) * TB + c * 1024 +
-                                                          ro.lane * 16), accs[s]);
+                if (gl * Gm::S + s < nlds) {
+#pragma unroll
+                  for (int c = 0; c < Gm::CH; ++c) accs[s] = mma(lat[m][c], lds_chunk(s, c), accs[s]);
+                }
+            }
             const int v = lv(gl);
             epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, pick_slot<Gm::S>(accs, ro.cslot), v,
                                               0xFFFFu - (uint32_t)(v - row0), lok(gl), 0.0f, bnl[gl][m], shi,
