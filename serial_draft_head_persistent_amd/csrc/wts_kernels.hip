@@ -1397,33 +1397,6 @@ __device__ __forceinline__ void make_noise(const WalkArgs& a, float* noise, int 
   }
 }
 
-// While wave 0 exchanges keys, wave 1 reads the embedding row of this
-// workgroup's local winner (one word per 128-byte line).  One of these rows
-// is the next step's latent; reading it now brings it into the device-side
-// cache, so the gather after the exchange does not wait for HBM.
-template <int WT, int HEAD, int TEMP, int NW>
-__device__ __forceinline__ void prefetch_rows(const WalkArgs& a, const unsigned long long* red, int row0,
-                                              int lane, char* lds_dummy) {
-  constexpr int LINES = HEAD == kHeadMarkov ? (WT == 0 ? 5 : 4) : 8;  // 128-byte lines per row
-  uint32_t acc = 0;
-  for (int q = lane; q < a.B * LINES; q += 64) {
-    const int b = q / LINES, j = q % LINES;
-    typename LKey<TEMP>::T lk = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) lk = kmax(lk, (typename LKey<TEMP>::T)red[ww * kMaxB + b]);
-    const int v = key_token(global_key(lk, row0));
-    if (v >= 0 && v < a.V) {
-      if (HEAD == kHeadMarkov && WT == 0)
-        acc ^= j < 4 ? *(const uint32_t*)(a.Eq + (size_t)v * 512 + j * 128) : __float_as_uint(a.Es[v]);
-      else if (HEAD == kHeadMarkov)
-        acc ^= *(const uint32_t*)(a.Eb + (size_t)v * kR + j * 64);
-      else
-        acc ^= __float_as_uint(a.E[(size_t)v * kR + j * 32]);
-    }
-  }
-  if (acc == 0x9E3779B9u) *lds_dummy = 1;  // keeps the loads; the byte is never read
-}
-
 // While wave 0 exchanges keys, other waves read one word of every 128-byte
 // line of the next step's base logits over this workgroup's rows.  The
 // non-register tiles load their base logits only one tile ahead of use; with
@@ -1794,7 +1767,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     stamp(t, 2);
     // the workgroup's log-sum-exp pairs of this step, merged during the exchange
     if (w > 0) lse_workgroup<WT, BB, NW, LS>(a, ro, w, ls, lred, lraw, lcnt, t, g, G);
-    if (!CAND && w == 1 && t + 1 < a.gamma) prefetch_rows<WT, HEAD, TEMP, NW>(a, red, row0, ro.lane, lds + kOffFlag + 4);
+    // (no reads of candidate rows during the exchange from two rows on: the
+    // exchange's hops slow down under memory traffic by more than the gather
+    // after it gains)
     if constexpr (CAND) {
       if (stage && w == 1 && t + 1 < a.gamma) stage_rows<HEAD, BB>(a, t, lds, a.timeout_ticks);
     }
