@@ -234,18 +234,26 @@ def graph_walks(head, t, n, **kw):
     return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
 
 
-def _stream_report(fit, plan, rf):
+def _stream_report(fit, plan, rf, phases=None):
     """Per-step streamed W bytes against the measured stream rates (HBM, and a
-    128 MiB working set in the memory-side cache)."""
+    128 MiB working set in the memory-side cache).  With the walk's phase
+    times, also the rate within the projection phase, the part of the step in
+    which the tiles stream (the gather and the exchange move no W)."""
     slope = fit["per_step_us"]
     gbps = plan["streamed_bytes"] / (slope * 1e-6) / 1e9
-    return {"per_step_us": round(slope, 3), "entry_us": round(fit["entry_us"], 2),
-            "median_us_g16": round(fit["median_us"][-1], 2),
-            "streamed_MB_per_step": round(plan["streamed_bytes"] / 1e6, 2),
-            "resident_MB": round(plan["resident_bytes"] / 1e6, 1),
-            "stream_GBps": round(gbps, 1),
-            "frac_of_hbm_measured": round(gbps / rf["hbm_read_GBps"], 4),
-            "frac_of_mall_measured": round(gbps / rf["mall_read_GBps"], 4)}
+    out = {"per_step_us": round(slope, 3), "entry_us": round(fit["entry_us"], 2),
+           "median_us_g16": round(fit["median_us"][-1], 2),
+           "streamed_MB_per_step": round(plan["streamed_bytes"] / 1e6, 2),
+           "resident_MB": round(plan["resident_bytes"] / 1e6, 1),
+           "stream_GBps": round(gbps, 1),
+           "frac_of_hbm_measured": round(gbps / rf["hbm_read_GBps"], 4),
+           "frac_of_mall_measured": round(gbps / rf["mall_read_GBps"], 4)}
+    if phases:
+        proj = phases["project_epilogue_reduce_us"]
+        g2 = plan["streamed_bytes"] / (proj * 1e-6) / 1e9
+        out.update({"projection_phase_us": proj, "stream_GBps_in_projection": round(g2, 1),
+                    "frac_of_hbm_measured_in_projection": round(g2 / rf["hbm_read_GBps"], 4)})
+    return out
 
 
 def walk_stats(us):
@@ -565,7 +573,7 @@ def main():
                "x0": torch.from_numpy(d16["x0"]).cuda()}
         pp = hp.plan(16)
         fp = fit_steps(hp, d16, t16, n=50, warmup=5)
-        extras["stream_int8_v151936_b16_partial"] = _stream_report(fp, pp, rf)
+        extras["stream_int8_v151936_b16_partial"] = _stream_report(fp, pp, rf, breakdown(hp, t16, reps=10))
         log("stream int8 partial", extras["stream_int8_v151936_b16_partial"])
         hp.close()
         head.close()
@@ -587,7 +595,7 @@ def main():
         log("bf16 248k", r3)
         # the partially resident sixteen-row walk against the stream rates
         f3 = fit_steps(h3, d3, t3, n=50, warmup=5)
-        extras["stream_bf16_v248320_b16"] = _stream_report(f3, h3.plan(16), rf)
+        extras["stream_bf16_v248320_b16"] = _stream_report(f3, h3.plan(16), rf, r3[-1]["phases"])
         log("stream bf16 248k B=16", extras["stream_bf16_v248320_b16"])
         h3.close()
         del t3, d3
