@@ -89,8 +89,9 @@ int noise_floats(const wts_ctx* ctx, int BB, int temperature) {
 // Tiles wave w of a workgroup with cnt tiles owns (every NW-th tile).
 int wave_tiles(int cnt, int w, int NW) { return cnt > w ? (cnt - w + NW - 1) / NW : 0; }
 
-// Residency plan for one batch bucket.  *full: the whole shard fits on chip
-// in the variant with more register tiles and LDS tiles allotted per wave.
+// Residency plan for one batch bucket.  *full: the variant with more register
+// tiles and LDS tiles allotted per wave, which holds the whole shard on chip,
+// chosen when the other cannot hold it or holds fewer tiles in registers.
 // Returns false if the kernel's LDS scratch (with the T=1 noise of one step)
 // does not fit in LDS.
 bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, wts_plan* p, int* lds_bytes,
@@ -113,7 +114,10 @@ bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, 
   bool whole = false;
   int lds_need = NW * lds;  // LDS tiles of the fullest workgroup
   const int regf = std::min(reg_tiles_full(ctx->head, ctx->wtype, BB), per_wave);
-  if (regf > 0 && exec == WTS_EXEC_RESIDENT && ctx->reg_cap < 0 && ctx->lds_cap < 0 && reg + lds < per_wave) {
+  // the whole-shard variant when the other cannot hold the shard, or when it
+  // holds more of it in registers (fewer LDS tiles; measured faster)
+  if (regf > 0 && exec == WTS_EXEC_RESIDENT && ctx->reg_cap < 0 && ctx->lds_cap < 0 &&
+      (reg + lds < per_wave || regf > reg)) {
     int need = 0, most = 0;
     for (int w = 0; w < NW; ++w) {
       const int rest = wave_tiles(per_wg, w, NW) - std::min(wave_tiles(per_wg, w, NW), regf);

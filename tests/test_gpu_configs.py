@@ -171,12 +171,14 @@ def test_last_row_start_and_reuse_across_walks():
 
 @pytest.mark.parametrize("B", [1, 2])
 def test_bf16_v151936_fully_resident(B):
-    # bf16 W at V = 151,936 (77.8 MB) stays on chip: 8 register + 2 LDS tiles per wave
+    # bf16 W at V = 151,936 (77.8 MB) stays on chip: the whole-shard variant, every tile of a
+    # wave in registers
     d = datagen.make_inputs(151936, 256, B, 16, wtype="bf16", seed=41)
     _case(test="bf16_v151936_resident", B=B, gamma=16)
     h, t = make_head(d)
     p = h.plan(B)
     assert p["stream_tiles"] == 0 and p["resident_bytes"] == p["w_bytes"] == 151936 * 512, p
+    assert p["lds_tiles"] == 0 and p["reg_tiles"] == p["tiles_per_wave"], p
     got = run(h, t)
     assert_bf16_close(got, oracle_walk(d, keep_z=True), f"bf16 152k B={B}", d=d)
     stream = run(h, t, exec="stream")
