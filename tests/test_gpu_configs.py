@@ -169,7 +169,7 @@ def test_last_row_start_and_reuse_across_walks():
 
 # ---- other residency points (Fig. 14 full case; int8 at the 248k vocabulary) ----
 
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("B", [1, 2, 4])
 def test_bf16_v151936_fully_resident(B):
     # bf16 W at V = 151,936 (77.8 MB) stays on chip: the whole-shard variant, every tile of a
     # wave in registers
