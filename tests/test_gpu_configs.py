@@ -186,6 +186,30 @@ def test_bf16_v151936_fully_resident(B):
     h.close()
 
 
+@pytest.mark.parametrize("wtype,B,T", [("bf16", 1, 0), ("bf16", 3, 1), ("int8", 1, 0), ("int8", 3, 1)])
+def test_ragged_vocabulary_on_chip(wtype, B, T):
+    # V = 200,003 is no multiple of the 16-row tile: the last tile holds 3 rows.
+    # bf16 takes the whole-shard kernel (13 tiles per wave: 11 in registers, the
+    # rest in LDS), int8 registers then LDS; three rows use the four-row bucket.
+    d = datagen.make_inputs(200003, 256, B, 8, wtype=wtype, seed=44)
+    _case(test="ragged_vocabulary_on_chip", wtype=wtype, B=B, T=T)
+    h, t = make_head(d)
+    p = h.plan(B, temperature=T)
+    # (resident bytes count whole tiles: the padded last tile makes them exceed V r)
+    assert p["stream_tiles"] == 0 and p["streamed_bytes"] == 0, p
+    if wtype == "bf16":
+        assert p["reg_tiles"] == 11, p
+    got = run(h, t, temperature=T, seed=8)
+    stream = run(h, t, exec="stream", temperature=T, seed=8)
+    assert np.array_equal(got["tokens"], stream["tokens"]) and np.array_equal(got["logits"], stream["logits"])
+    ref = oracle_walk(d, temperature=T, seed=8, keep_z=wtype == "bf16")
+    if wtype == "int8":
+        assert_exact(got, ref, f"ragged int8 B={B} T={T}")
+    else:
+        assert_bf16_close(got, ref, f"ragged bf16 B={B} T={T}", d=d, temperature=T, seed=8)
+    h.close()
+
+
 @pytest.mark.parametrize("B,T", [(1, 0), (1, 1), (4, 0)])
 def test_int8_v248320_fully_resident_exact(B, T):
     # int8 W at V = 248,320 (63.6 MB) stays on chip: registers, then LDS

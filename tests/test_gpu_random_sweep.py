@@ -12,7 +12,7 @@ import pytest
 import datagen
 from gpu_helpers import make_head, run, oracle_walk, assert_exact, assert_bf16_close
 
-N_CASES = 24
+N_CASES = 48
 
 
 def _draw(i):
