@@ -147,8 +147,8 @@ def step_rooflines(plan, V, r, B, fit, rf):
     registers or LDS; the busiest SIMD issues r/64 int8 MFMAs per tile of its
     share, at the measured MFMA rate.  On-chip operand rate, aggregate: the W
     bytes of one step against the measured rate at which all CUs' MFMAs take
-    B operands (1 KiB per MFMA) and LDS delivers reads (the north-star's
-    resident-bandwidth roofline).  Step floor: that bound plus one
+    B operands (1 KiB per MFMA) and LDS delivers reads (the resident-bandwidth
+    roofline: resident steps against aggregate on-chip read bandwidth).  Step floor: that bound plus one
     cross-workgroup selection round measured in isolation.  Entry: the shard's
     one-time load against the measured HBM rate."""
     G = rf["grid"]
@@ -408,7 +408,7 @@ def main():
         summarize_counters(args.summarize_counters, kernel=args.kernel)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 "
+        print(json.dumps({"error": "the walk runs on one GPU only; run with --gpus 1 "
                           "(the walk's vocabulary sharding over several GPUs is a design note, not built)"}))
         sys.exit(2)
     import torch
