@@ -107,6 +107,7 @@ struct WalkArgs {
   int head;
   int reg_tiles;           // per wave, in registers
   int lds_tiles;           // per wave, in LDS
+  int lds_extra;           // waves 0 .. lds_extra - 1 hold one LDS tile more (walks that stream)
   int noise_off;           // T=1 persistent Markov walks: LDS offset of the noise rows, else 0
   int noise_stride;        // floats per batch row in that buffer (>= rows of a workgroup)
   // of this walk

@@ -1453,7 +1453,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   const int cnt = te - tb;
   const int nw = cnt > w ? (cnt - w + NW - 1) / NW : 0;
   const int nreg = min(nw, a.reg_tiles);
-  const int nlds = FULL ? min(nw - nreg, kFullLdsMax) : min(nw - nreg, a.lds_tiles);
+  const int nlds = FULL ? min(nw - nreg, kFullLdsMax) : min(nw - nreg, a.lds_tiles + (w < a.lds_extra ? 1 : 0));
   Ctrl* ctrl = a.ctrl;
   // The walk's epoch and the first state are requested before the shard, so
   // that their latency overlaps the shard load instead of preceding it.
@@ -1470,7 +1470,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   float2* lraw = lred + kWaves * kMaxB;                           // [entries][64]
   int* lcnt = (int*)(lds + kOffLseCnt);
   const int scratch = lds_scratch_bytes(HEAD, WT, BB) + (NOISE ? BB * a.noise_stride * 4 : 0);
-  int lds_before = w * a.lds_tiles;  // LDS tiles of the waves before this one
+  int lds_before = w * a.lds_tiles + min(w, a.lds_extra);  // LDS tiles of the waves before this one
   if (FULL) {
     lds_before = 0;
     for (int u = 0; u < w; ++u) {

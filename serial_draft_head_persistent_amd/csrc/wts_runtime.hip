@@ -95,7 +95,8 @@ int wave_tiles(int cnt, int w, int NW) { return cnt > w ? (cnt - w + NW - 1) / N
 // Returns false if the kernel's LDS scratch (with the T=1 noise of one step)
 // does not fit in LDS.
 bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, wts_plan* p, int* lds_bytes,
-               int* noise_off = nullptr, int* noise_stride = nullptr, int* full = nullptr) {
+               int* noise_off = nullptr, int* noise_stride = nullptr, int* full = nullptr,
+               int* lds_extra = nullptr) {
   const int per_wg = (ctx->tiles + ctx->grid - 1) / ctx->grid;
   const int NW = waves_for(ctx->head, ctx->wtype);
   const int per_wave = (per_wg + NW - 1) / NW;
@@ -131,6 +132,13 @@ bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, 
       lds_need = need;
     }
   }
+  // a walk that streams: the whole tiles that still fit in LDS go one each to
+  // the first waves (those with the most tiles), so that fewer tiles stream
+  int extra = 0;
+  if (!whole && exec == WTS_EXEC_RESIDENT && ctx->lds_cap < 0 && reg + lds < per_wave)
+    extra = std::max(0, std::min(NW - 1, (kLdsMax - scratch) / tb - NW * lds));
+  lds_need += extra;
+  if (lds_extra) *lds_extra = extra;
   if (full) *full = whole ? 1 : 0;
   p->grid = ctx->grid;
   p->waves = NW;
@@ -138,12 +146,13 @@ bool make_plan(const wts_ctx* ctx, int BB, int exec, int temperature, bool lse, 
   p->tiles_per_wave = per_wave;
   p->reg_tiles = reg;
   p->lds_tiles = lds;
-  p->stream_tiles = whole ? 0 : per_wave - reg - lds;
+  p->stream_tiles = whole ? 0 : per_wave - reg - lds - (extra > 0 ? 1 : 0);
   // exact on-chip bytes: count each wave's tiles
   long long res_tiles = 0;
   for (int g = 0; g < ctx->grid; ++g) {
     const int cnt = (int)((long long)(g + 1) * ctx->tiles / ctx->grid) - (int)((long long)g * ctx->tiles / ctx->grid);
-    for (int w = 0; w < NW; ++w) res_tiles += whole ? wave_tiles(cnt, w, NW) : std::min(wave_tiles(cnt, w, NW), reg + lds);
+    for (int w = 0; w < NW; ++w)
+      res_tiles += whole ? wave_tiles(cnt, w, NW) : std::min(wave_tiles(cnt, w, NW), reg + lds + (w < extra ? 1 : 0));
   }
   const long long esz = ctx->wtype == WTS_W_INT8 ? 1 : 2;
   p->w_bytes = (long long)ctx->V * kR * esz;
@@ -401,9 +410,9 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   const int BB = batch_bucket(p->B);
   wts_plan plan;
   int lds_bytes = 0;
-  int noise_off = 0, noise_stride = 0, full = 0;
+  int noise_off = 0, noise_stride = 0, full = 0, lds_extra = 0;
   if (!make_plan(ctx, BB, p->exec, p->temperature, p->lse_out != nullptr, &plan, &lds_bytes, &noise_off,
-                 &noise_stride, &full))
+                 &noise_stride, &full, &lds_extra))
     return WTS_ERR_UNSUPPORTED;
 
   WalkArgs a{};
@@ -421,6 +430,7 @@ wts_status walk_impl(wts_ctx* ctx, const wts_walk_params* p, Ctrl* ctrl, float* 
   a.head = ctx->head;
   a.reg_tiles = plan.reg_tiles;
   a.lds_tiles = plan.lds_tiles;
+  a.lds_extra = lds_extra;
   a.noise_off = noise_off;
   a.noise_stride = noise_stride;
   a.B = p->B;
