@@ -29,7 +29,7 @@ constexpr int waves_for(int head, int wtype) { return (head == 0 && wtype == 1) 
 constexpr int reg_tiles_max(int head, int wtype, int BB, int temp, bool ls) {
   return wtype == 0 ? (head == 0 ? (BB == 1 ? 5 : BB <= 8 ? (temp == 0 && !ls ? 5 : 4) : 2)
                                  : (BB == 1 ? 5 : BB == 2 ? 4 : BB == 4 ? 3 : BB == 8 ? 2 : 1))
-                    : waves_for(head, wtype) == 4 ? (BB == 1 ? 9 : BB == 2 ? 8 : BB <= 4 ? (temp == 0 && !ls ? 8 : 7) : BB == 8 ? (temp == 0 && !ls ? 7 : 6) : (temp == 0 && !ls ? 6 : 5)) : 1;
+                    : waves_for(head, wtype) == 4 ? (BB == 1 ? 9 : BB == 2 ? 8 : BB <= 4 ? (temp == 0 && !ls ? 8 : 7) : BB == 8 ? (temp == 0 && !ls ? 7 : 6) : (temp == 0 && !ls ? 7 : 5)) : 1;
 }
 // Register tiles per wave of the whole-shard-on-chip variant (bf16 Markov
 // walks of up to four batch rows): without streaming buffers a wave can hold
