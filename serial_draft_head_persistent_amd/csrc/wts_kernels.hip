@@ -1592,7 +1592,12 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
   __syncthreads();
   if (*sflag) return;
   fetch_base(0);
-  if (HEAD == kHeadRecurrent) recurrent_matvec<BB>(a, tid, lds, racc);
+  if (HEAD == kHeadRecurrent) {
+    recurrent_matvec<BB>(a, tid, lds, racc);
+    // every wave has read h_0 before step 0 overwrites it with h_1 (later
+    // steps have the end-of-step barrier between the two)
+    __syncthreads();
+  }
   if (HEAD == kHeadMarkov && CAND && fixed) {
     // the probe's latent, staged once where later steps read staged rows
     if (tid < 32)

@@ -138,6 +138,24 @@ def test_config4_recurrent_full_size_exact():
     h.close()
 
 
+@pytest.mark.parametrize("wtype", ["int8", "bf16"])
+def test_recurrent_first_step_repeated(wtype):
+    # Step 0 of a recurrent walk reads the sums A h_0 made before the loop and
+    # then replaces h_0 by h_1 in LDS: repeated short walks at sixteen rows
+    # (the longest sums) must each match the oracle.
+    d = datagen.make_inputs(48915, 256, 16, 2, wtype=wtype, head="recurrent", seed=61)
+    _case(recurrent=wtype, B=16, gamma=2, repeats=8)
+    h, t = make_head(d)
+    ref = oracle_walk(d, keep_z=wtype == "bf16")
+    for r in range(8):
+        got = run(h, t)
+        if wtype == "int8":
+            assert_exact(got, ref, f"recurrent int8 repeat {r}")
+        else:
+            assert_bf16_close(got, ref, f"recurrent bf16 repeat {r}", d=d, max_total=16)
+    h.close()
+
+
 @pytest.mark.parametrize("V", [1, 15, 16, 33])
 def test_tiny_vocab(V):
     d = datagen.make_inputs(V, 256, 2, 3, seed=40 + V)
