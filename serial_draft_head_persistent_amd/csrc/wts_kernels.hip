@@ -359,6 +359,15 @@ constexpr int kRecRowBytes = kR * 4;
 #ifndef WTS_PIN_FULL
 #define WTS_PIN_FULL 7
 #endif
+#ifndef WTS_LDS_RING_1
+#define WTS_LDS_RING_1 8
+#endif
+#ifndef WTS_LDS_RING_2
+#define WTS_LDS_RING_2 4
+#endif
+#ifndef WTS_LDS_RING_4
+#define WTS_LDS_RING_4 2
+#endif
 
 // Raw buffer resource over [p, p + bytes): loads at byte offsets >= bytes
 // return 0.  Word 3 as for untyped loads on gfx9 (32-bit data format).
@@ -1718,7 +1727,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     }
     // LDS-resident and streamed tiles
     if (FULL) {
-      // LDS tiles only, S per group, their chunks read straight into the MFMA operands
+      // LDS tiles only, S per group, their chunks read straight into the MFMA operands,
+      // LR reads in flight (as many as the registers left over allow)
+      constexpr int LR = BB == 1 ? WTS_LDS_RING_1 : BB == 2 ? WTS_LDS_RING_2 : WTS_LDS_RING_4;
 #pragma unroll
       for (int gl = 0; gl < NLG; ++gl) {
         if (gl * Gm::S < nlds) {
@@ -1732,18 +1743,31 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
               return *(const v4i*)(ldsw + (size_t)(gl * Gm::S + s) * TB + c * 1024 + ro.lane * 16);
             };
             if ((gl + 1) * Gm::S <= nlds) {
-              // a full group: chunk-major, no per-MFMA test
+              // a full group: chunk-major, no per-MFMA test; the chunk reads run
+              // LR ahead of the MFMAs that take them (read, wait, multiply one
+              // chunk at a time costs a whole LDS round trip per MFMA)
+              constexpr int NJ = Gm::CH * Gm::S;
+              v4i ring[LR];
 #pragma unroll
-              for (int c = 0; c < Gm::CH; ++c)
+              for (int j = 0; j < LR; ++j) ring[j] = lds_chunk(j % Gm::S, j / Gm::S);
 #pragma unroll
-                for (int s = 0; s < Gm::S; ++s) accs[s] = mma(lat[m][c], lds_chunk(s, c), accs[s]);
+              for (int j = 0; j < NJ; ++j) {
+                accs[j % Gm::S] = mma(lat[m][j / Gm::S], ring[j % LR], accs[j % Gm::S]);
+                if (j + LR < NJ) ring[j % LR] = lds_chunk((j + LR) % Gm::S, (j + LR) / Gm::S);
+              }
             } else {
-              // the last, partial group: one test per tile
+              // the last, partial group: one test per tile, its chunks read ahead the same way
 #pragma unroll
               for (int s = 0; s < Gm::S; ++s)
                 if (gl * Gm::S + s < nlds) {
+                  v4i ring[LR];
 #pragma unroll
-                  for (int c = 0; c < Gm::CH; ++c) accs[s] = mma(lat[m][c], lds_chunk(s, c), accs[s]);
+                  for (int c = 0; c < LR; ++c) ring[c] = lds_chunk(s, c);
+#pragma unroll
+                  for (int c = 0; c < Gm::CH; ++c) {
+                    accs[s] = mma(lat[m][c], ring[c % LR], accs[s]);
+                    if (c + LR < Gm::CH) ring[c % LR] = lds_chunk(s, c + LR);
+                  }
                 }
             }
             const int v = lv(gl);
