@@ -1509,7 +1509,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     asm volatile("" : "+v"(v));
     return v;
   };
-  auto gok = [&](int gi) { return gi * Gm::S + ro.cslot < nreg && gv(gi) < a.V; };
+  // (both tests evaluated, without a short circuit: the opaque row cannot be
+  // computed speculatively, so `&&` would put each group's test under a branch)
+  auto gok = [&](int gi) { return (gi * Gm::S + ro.cslot < nreg) & (gv(gi) < a.V); };
   float gsw[WT == 0 ? Gm::NG : 1];  // row scales of the register groups (int8)
 #pragma unroll
   for (int gi = 0; gi < (WT == 0 ? Gm::NG : 1); ++gi)  // rows past the padded scales read 0
@@ -1535,7 +1537,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     asm volatile("" : "+v"(v));
     return v;
   };
-  auto lok = [&](int gl) { return gl * Gm::S + ro.cslot < nlds && lv(gl) < a.V; };
+  auto lok = [&](int gl) { return (gl * Gm::S + ro.cslot < nlds) & (lv(gl) < a.V); };
   uint16_t bnl[NLG][Gm::NM][Gm::NE];
   auto fetch_base = [&](int t) {
 #pragma unroll
