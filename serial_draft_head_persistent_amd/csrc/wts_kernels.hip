@@ -612,7 +612,10 @@ struct LseAcc<NM, NE, false> {
 // With NZ, T=1 noise comes from LDS (computed one step ahead):
 // noise[b * a.noise_stride + (v - row0)], row0 = the workgroup's first row.
 // With LS, the logit also enters the running log-sum-exp pairs.
-template <int WT, int BB, int TEMP, bool NZ, bool LS, bool GP = false>
+// With BS, the logit is written by a buffer store whose offset lies past the
+// end when nothing is to be written (such stores are dropped), so the epilogue
+// has no branch and the scheduler can interleave it with the next group's MFMAs.
+template <int WT, int BB, int TEMP, bool NZ, bool LS, bool GP = false, bool BS = false>
 __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>& ro, int t, int m,
                                          const typename AccT<WT>::T& acc, int v, uint32_t lrow, bool ok,
                                          float sw, const uint16_t (&bv)[Geo<WT, BB>::NE],
@@ -639,7 +642,13 @@ __device__ __forceinline__ void epilogue(const WalkArgs& a, const Roles<WT, BB>&
     // bf16 rounding to nearest even: the upper half of r is the logit
     const uint32_t zb = __float_as_uint(z);
     const uint32_t r = zb + 0x7FFFu + ((zb >> 16) & 1u);
-    if (a.logits != nullptr) {  // uniform: skipped entirely when logits are not requested
+    if constexpr (BS) {
+      // the logits have the shape of the base logits: the same 32-bit byte offsets
+      const uint32_t off = okb ? 2u * (((uint32_t)b * (uint32_t)a.gamma + (uint32_t)t) * (uint32_t)a.V + (uint32_t)v)
+                               : 0xFFFFFFFEu;
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(r >> 16),
+                                            buf_rsrc(a.logits, a.logits != nullptr ? a.base_bytes : 0u), off, 0, 0);
+    } else if (a.logits != nullptr) {  // uniform: skipped entirely when logits are not requested
       if (okb) a.logits[((size_t)b * a.gamma + t) * a.V + v] = (uint16_t)(r >> 16);
     }
     const float lf = __uint_as_float(r & 0xFFFF0000u);  // the logit, widened exactly
@@ -1694,7 +1703,9 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
     // projection over the register-resident tiles, S tiles per accumulator
 #pragma unroll
     for (int gi = 0; gi < Gm::NG; ++gi) {
-      if (gi * Gm::S < nreg) {
+      // (whole-shard kernels: every group, so that the groups and their
+      // epilogues form one block; a slot past the wave's tiles is dropped by gok)
+      if (FULL || gi * Gm::S < nreg) {
 #pragma unroll
         for (int m = 0; m < Gm::NM; ++m) {
           // One accumulator per tile of the group (independent MFMA chains).
@@ -1721,7 +1732,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
             }
           AT acc = pick_slot<Gm::S>(accs, ro.cslot);
           if (SPLIT) acc = acc + acc2;
-          epilogue<WT, BB, TEMP, NOISE, LS, GP>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
+          epilogue<WT, BB, TEMP, NOISE, LS, GP, FULL>(a, ro, t, m, acc, gv(gi), 0xFFFFu - (uint32_t)(gv(gi) - row0),
                                                 gok(gi), WT == 0 ? gsw[gi] : 0.0f, bnx[gi][m], shi, best, ls,
                                                 noise, row0, gzp[GP ? gi : 0][m]);
         }
@@ -1773,7 +1784,7 @@ __global__ __launch_bounds__(waves_for(HEAD, WT) * 64, 1) void walk_kernel(WalkA
                 }
             }
             const int v = lv(gl);
-            epilogue<WT, BB, TEMP, NOISE, LS>(a, ro, t, m, pick_slot<Gm::S>(accs, ro.cslot), v,
+            epilogue<WT, BB, TEMP, NOISE, LS, false, true>(a, ro, t, m, pick_slot<Gm::S>(accs, ro.cslot), v,
                                               0xFFFFu - (uint32_t)(v - row0), lok(gl), 0.0f, bnl[gl][m], shi,
                                               best, ls, noise, row0);
           }
